@@ -1,0 +1,87 @@
+"""The CPU oracle against its pins (no GPU).
+
+Every pin in oracle_pins.py must hold for the oracle as committed, and each
+planted mistake below (made in a private copy of oracle_gemm.c, compiled on
+the CPU) must break at least one pin: that is what shows the pins would
+catch a dropped term, a wrong sign or index, a transposed operand, a wrong
+decoder or a wrong integer wrap.
+"""
+import os
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+
+@pytest.fixture(scope="module")
+def orc():
+    oracle.build()
+    return oracle.OracleLib(oracle.lib_path())
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(orc, pin):
+    pin(orc)
+
+
+def test_oracle_rejects_bad_arguments(orc):
+    a = np.zeros((2, 3), dtype=np.float32)
+    b = np.zeros((3, 4), dtype=np.float32)
+    with pytest.raises(ValueError):
+        orc.gemm(a, np.zeros((2, 4), dtype=np.float32), "f32", "RR")  # K mismatch
+    with pytest.raises(TypeError):
+        orc.gemm(a, b.astype(np.float64), "f32", "RR")
+    with pytest.raises(ValueError):
+        orc.gemm(a, b, "f64", "RR")
+    with pytest.raises(ValueError):
+        orc.gemm_entries(a, b, "f32", "RR", [2], [0])  # row out of range
+
+
+def test_oracle_empty_shapes(orc):
+    for dtype, npt in (("i8", np.int8), ("f32", np.float32)):
+        c = orc.gemm(np.zeros((0, 5), npt), np.zeros((5, 3), npt), dtype, "RR")
+        assert c.shape == (0, 3)
+        c = orc.gemm(np.zeros((4, 0), npt), np.zeros((3, 0), npt), dtype, "RC")
+        assert c.shape == (4, 3) and np.all(c == 0)
+
+
+# (description, text in oracle_gemm.c, replacement, occurrences expected)
+MUTANTS = [
+    ("dropped last k term", "k < K; ++k)", "k < K - 1; ++k)", None),
+    ("B layouts swapped", "k * ldb + j : j * ldb + k", "j * ldb + k : k * ldb + j", 1),
+    ("wrong sign in RC float sum", "s += arow[k] *", "s -= arow[k] *", 1),
+    ("wrong fp16 exponent bias", "e - 25)", "e - 24)", 1),
+    ("wrong bf16 placement", "(uint32_t)b << 16", "(uint32_t)b << 15", 1),
+    ("wrong int32 wrap", "& 0xffffffffu", "& 0x7fffffffu", 1),
+    ("RR row uses column of A", "load_f(dtype, A, i * lda + k);\n                    for",
+     "load_f(dtype, A, i * lda + (k ? k - 1 : 0));\n                    for", 1),
+    ("first term dropped in RR int loop", "acc[j] += aik * (int64_t)brow[j]",
+     "acc[j] += (k ? aik : 0) * (int64_t)brow[j]", 1),
+]
+
+
+@pytest.mark.parametrize("desc,old,new,count", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(desc, old, new, count):
+    src = open(oracle.SRC).read()
+    n = src.count(old)
+    assert n >= 1 and (count is None or n == count), (desc, n)
+    tmp = tempfile.mkdtemp(prefix="oracle_mutant_")
+    try:
+        path = os.path.join(tmp, "mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.build(src=path, out=os.path.join(tmp, "libmutant.so"))
+        mutant = oracle.OracleLib(lib)
+        failed = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(mutant)
+            except AssertionError:
+                failed.append(pin.__name__)
+        assert failed, "no pin caught: " + desc
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
