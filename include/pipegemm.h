@@ -1,0 +1,145 @@
+/*
+ * pipegemm.h -- C ABI of the software-pipelined tiled GEMM for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Operation.  gemm_run computes C = A * B,
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N,
+ * the product the "CUDA Kernel Study: Pipelining" README benchmarks (Example
+ * Code: "C = A x B") and that "Part 4 -- Pipelining and Occupancy"
+ * (gpucourse.com) writes out as the triple loop of section 4.3.  The K loop
+ * runs over BK-wide tiles restructured into prologue / main loop / epilogue
+ * so that the global->LDS copy of the next tile overlaps the matrix-core
+ * work on the current one ("pipeline-gpu-kernel", step 3; the README's
+ * ping-pong and multi-stage cases).  Pipelining reorders loads only; the
+ * arithmetic is that of the unpipelined loop ("pipeline-gpu-kernel", step 5).
+ *
+ * Element types (input -> accumulator -> output):
+ *   GEMM_I8   int8  -> int32 (exact; wraps modulo 2^32 like the uint32_t
+ *                     reference at the end of the gpucourse section 4.3)
+ *   GEMM_F16  fp16  -> fp32  -> fp16 (round to nearest even)
+ *   GEMM_BF16 bf16  -> fp32  -> bf16 (round to nearest even)
+ *   GEMM_F32  fp32  -> fp32  -> fp32
+ *
+ * Layouts (leading dimensions are in elements):
+ *   A is always row-major M x K:  A(i,k) = A[i*lda + k], lda >= K.
+ *   GEMM_LAYOUT_RR: B row-major K x N:     B(k,j) = B[k*ldb + j], ldb >= N.
+ *   GEMM_LAYOUT_RC: B column-major K x N:  B(k,j) = B[j*ldb + k], ldb >= K.
+ *   C is always row-major M x N:  C(i,j) = C[i*ldc + j], ldc >= N.
+ *
+ * Pipeline depth and load path:
+ *   stages in [1, 4].
+ *   GEMM_VARIANT_DIRECT: global -> LDS copies that bypass registers (the
+ *     README's cp.async case; here the LDS-DMA form of buffer loads).  An
+ *     LDS ring of `stages` slots with stages-1 tiles in flight; stages = 1 is
+ *     the serial load-sync-compute-sync loop of the README's Background.
+ *   GEMM_VARIANT_REG: global -> VGPR -> LDS (the README's ping-pong case).
+ *     min(stages, 2) LDS slots and max(1, stages-1) register staging sets,
+ *     each a tile in flight; stages = 1 is the skill's register-only prefetch
+ *     into a single buffer (step 1, "if it fails"), stages = 2 the classic
+ *     double buffer.
+ *   For a fixed dtype, layout and tile every (stages, variant) pair issues
+ *   the same matrix-core instructions in the same k order, so all of them
+ *   return bit-identical C.
+ *
+ * Memory ownership.  The caller allocates, owns and frees A, B, C and the
+ * stream; they are device pointers (hipMalloc or torch CUDA tensors) on the
+ * handle's device.  The library allocates no device memory.  A and B are
+ * only read.  C must not overlap A or B.
+ *
+ * Errors.  Every entry point returns GEMM_OK (0) or one of the codes below;
+ * nothing is thrown across the ABI.  Argument checks run before any HIP call,
+ * so a rejected call has no side effect.  gemm_run is asynchronous: it
+ * enqueues on `stream` and returns; faults during execution surface at the
+ * caller's next synchronisation of that stream.
+ */
+#ifndef PIPEGEMM_H
+#define PIPEGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_I8 = 0, GEMM_F16 = 1, GEMM_BF16 = 2, GEMM_F32 = 3 } gemm_dtype_t;
+typedef enum { GEMM_LAYOUT_RR = 0, GEMM_LAYOUT_RC = 1 } gemm_layout_t;
+typedef enum { GEMM_VARIANT_REG = 0, GEMM_VARIANT_DIRECT = 1 } gemm_variant_t;
+
+enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,  /* NULL handle/pointer, negative size, bad enum,
+                                  leading dimension too small, stages not in [1,4] */
+    GEMM_ERR_ALIGNMENT = 2,    /* a base pointer not 16-byte aligned, lda/ldb/ldc
+                                  times the element size not a multiple of 16 B,
+                                  or K (and N for layout RR) not a multiple of
+                                  16 B worth of elements */
+    GEMM_ERR_UNSUPPORTED = 3,  /* no kernel instance fits the LDS budget, or an
+                                  operand tile row span exceeds 2^31 bytes */
+    GEMM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch
+                                  failure); see gemm_last_hip_error */
+};
+
+/* Tile classes selectable with gemm_set_tile (GEMM_TILE_AUTO lets the
+ * library choose the largest tile that still gives at least one workgroup
+ * per compute unit). */
+enum { GEMM_TILE_AUTO = -1, GEMM_TILE_256x256 = 0, GEMM_TILE_128x128 = 1, GEMM_TILE_32x64 = 2 };
+
+typedef struct gemm_handle_s *gemm_handle_t;
+
+/* What gemm_run would launch for a given call (see gemm_query). */
+typedef struct {
+    int32_t tile;            /* GEMM_TILE_* actually chosen */
+    int32_t block_m, block_n, block_k;
+    int32_t waves_m, waves_n;
+    int32_t threads;         /* per workgroup */
+    int32_t lds_slots;       /* slots of the LDS ring */
+    int32_t reg_sets;        /* VGPR staging sets (0 for the direct variant) */
+    int32_t tiles_in_flight; /* K-tiles loading while one is multiplied */
+    int32_t lds_bytes;       /* LDS per workgroup */
+    int32_t loads_per_tile;  /* 16-byte loads per lane per K-tile */
+    int64_t grid;            /* workgroups */
+    int64_t k_tiles;         /* ceil(K / block_k) */
+    int32_t k_tail;          /* K mod block_k; 0 means no ragged last tile */
+    int32_t reserved;
+} gemm_config_info_t;
+
+/* Bind a handle to HIP device `device`.  Allocates host memory for the
+ * handle only.  Returns GEMM_ERR_INVALID_ARG for a NULL `out` or a negative
+ * device, GEMM_ERR_HIP when the device does not exist. */
+int gemm_create(gemm_handle_t *out, int device);
+
+/* C = A * B on `stream` (a hipStream_t; NULL is the null stream).  Argument
+ * checks as described above; M, N or K may be 0 (M or N = 0 does nothing,
+ * K = 0 writes C = 0).  Launches on the handle's device. */
+int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+             int dtype, int layout, int stages, int variant,
+             const void *A, int64_t lda, const void *B, int64_t ldb,
+             void *C, int64_t ldc, void *stream);
+
+/* Release a handle.  NULL is a no-op.  Does not synchronise any stream. */
+int gemm_destroy(gemm_handle_t h);
+
+/* Force a tile class for later gemm_run calls on this handle
+ * (GEMM_TILE_AUTO restores the automatic choice). */
+int gemm_set_tile(gemm_handle_t h, int tile);
+
+/* The configuration gemm_run would use, after the same argument checks, with
+ * no HIP call and no device access.  Pointers are never dereferenced: a
+ * non-NULL pointer is checked for alignment, a NULL one is taken as "not
+ * given" and skipped.  The tile is chosen for a 256-CU device (MI355X).
+ * `tile` is a GEMM_TILE_* value. */
+int gemm_query(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+               int variant, int tile, const void *A, int64_t lda, const void *B,
+               int64_t ldb, const void *C, int64_t ldc, gemm_config_info_t *info);
+
+/* Static text for a status code (never NULL). */
+const char *gemm_status_string(int status);
+
+/* The last hipError_t seen by this thread's failing call (0 if none). */
+int gemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIPEGEMM_H */

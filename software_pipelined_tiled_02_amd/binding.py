@@ -1,0 +1,179 @@
+"""Thin ctypes binding of libpipegemm.so (the C ABI in include/pipegemm.h).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels.
+The functions keep the C names; device buffers are passed as torch CUDA
+tensors (their data_ptr) or plain integer addresses.  There is no fallback:
+if the library is missing, loading raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpipegemm.so")
+
+GEMM_I8, GEMM_F16, GEMM_BF16, GEMM_F32 = 0, 1, 2, 3
+GEMM_LAYOUT_RR, GEMM_LAYOUT_RC = 0, 1
+GEMM_VARIANT_REG, GEMM_VARIANT_DIRECT = 0, 1
+GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_ALIGNMENT, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP = 0, 1, 2, 3, 4
+GEMM_TILE_AUTO, GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_32x64 = -1, 0, 1, 2
+
+DTYPES = {"i8": GEMM_I8, "f16": GEMM_F16, "bf16": GEMM_BF16, "f32": GEMM_F32}
+LAYOUTS = {"RR": GEMM_LAYOUT_RR, "RC": GEMM_LAYOUT_RC}
+VARIANTS = {"reg": GEMM_VARIANT_REG, "direct": GEMM_VARIANT_DIRECT}
+TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_TILE_128x128,
+         "32x64": GEMM_TILE_32x64}
+
+# C functions exported by the library (the names include/pipegemm.h declares)
+EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",
+           "gemm_status_string", "gemm_last_hip_error")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = "%s: %s" % (where, gemm_status_string(status))
+        if status == GEMM_ERR_HIP:
+            msg += " (hipError %d)" % _lib().gemm_last_hip_error()
+        super().__init__(msg)
+
+
+class ConfigInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "tile", "block_m", "block_n", "block_k", "waves_m", "waves_n", "threads", "lds_slots",
+        "reg_sets", "tiles_in_flight", "lds_bytes", "loads_per_tile")] + [
+        ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
+        ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpipegemm.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.gemm_create.argtypes = [ctypes.POINTER(vp), ci]
+        lib.gemm_create.restype = ci
+        lib.gemm_run.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64, vp]
+        lib.gemm_run.restype = ci
+        lib.gemm_destroy.argtypes = [vp]
+        lib.gemm_destroy.restype = ci
+        lib.gemm_set_tile.argtypes = [vp, ci]
+        lib.gemm_set_tile.restype = ci
+        lib.gemm_query.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
+                                   ctypes.POINTER(ConfigInfo)]
+        lib.gemm_query.restype = ci
+        lib.gemm_status_string.argtypes = [ci]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_last_hip_error.argtypes = []
+        lib.gemm_last_hip_error.restype = ci
+        _L = lib
+    return _L
+
+
+def library():
+    """The loaded ctypes library (loads it on first call)."""
+    return _lib()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _enum(x, table):
+    return table[x] if isinstance(x, str) else int(x)
+
+
+def gemm_status_string(status):
+    return _lib().gemm_status_string(int(status)).decode()
+
+
+def gemm_create(device=0):
+    h = ctypes.c_void_p()
+    rc = _lib().gemm_create(ctypes.byref(h), int(device))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_create")
+    return h
+
+
+def gemm_destroy(h):
+    _lib().gemm_destroy(h)
+
+
+def gemm_set_tile(h, tile):
+    rc = _lib().gemm_set_tile(h, _enum(tile, TILES))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_set_tile")
+
+
+def gemm_run(h, M, N, K, dtype, layout, stages, variant, A, lda, B, ldb, C, ldc, stream=None,
+             check=True):
+    """Enqueue C = A * B; returns the status (raises on error when check)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    rc = _lib().gemm_run(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
+                         _enum(variant, VARIANTS), _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, stream)
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_run")
+    return rc
+
+
+def gemm_query(M, N, K, dtype, layout, stages, variant, tile="auto", A=0, lda=None, B=0,
+               ldb=None, C=0, ldc=None, check=True):
+    """The configuration gemm_run would use (no HIP call).  Returns (status, dict)."""
+    layout_v = _enum(layout, LAYOUTS)
+    lda = K if lda is None else lda
+    ldb = (N if layout_v == GEMM_LAYOUT_RR else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    info = ConfigInfo()
+    rc = _lib().gemm_query(M, N, K, _enum(dtype, DTYPES), layout_v, int(stages),
+                           _enum(variant, VARIANTS), _enum(tile, TILES), A, lda, B, ldb, C, ldc,
+                           ctypes.byref(info))
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_query")
+    return rc, info.as_dict()
+
+
+class Gemm:
+    """Owns a handle; ``run`` takes torch CUDA tensors in the ABI's storage:
+    A (M x K row-major), B (K x N row-major for RR, its N x K transpose for
+    RC), C (M x N row-major)."""
+
+    def __init__(self, device=0):
+        self.h = gemm_create(device)
+
+    def close(self):
+        if self.h is not None:
+            gemm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_tile(self, tile):
+        gemm_set_tile(self.h, tile)
+
+    def run(self, a, b, c, dtype, layout, stages, variant, stream=None):
+        M, K = a.shape
+        N = b.shape[1] if _enum(layout, LAYOUTS) == GEMM_LAYOUT_RR else b.shape[0]
+        for t in (a, b, c):
+            if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+                raise ValueError("operands must be 2-D with unit stride along the last axis")
+        return gemm_run(self.h, M, N, K, dtype, layout, stages, variant,
+                        a, a.stride(0), b, b.stride(0), c, c.stride(0), stream)

@@ -1,0 +1,242 @@
+// abi.hip -- the C ABI declared in include/pipegemm.h: argument checks,
+// configuration choice (tile class, K-tile, LDS ring, staging sets) and the
+// kernel launch.  Host code only; the kernels live in kernels_*.hip.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "pipegemm.h"
+#include "kernel_args.h"
+#include "tile_layout.h"
+
+struct gemm_handle_s {
+    int device;
+    int num_cus;
+    int tile_override;  // GEMM_TILE_AUTO or a class
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kDefaultCus = 256;  // MI355X; used when no device is at hand
+
+struct Plan {
+    gemm_config_info_t info;
+    int tile;
+    int64_t tiles_m, tiles_n;
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool instance_exists(int layout, int tile) {
+    // layout RR is built at the 128x128 and 32x64 tiles only
+    return layout == pg::LAYOUT_RC || tile != pg::TILE_L;
+}
+
+// Every check of the ABI, then the configuration.  No HIP call.
+int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
+              int tile, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+              int64_t ldc, int num_cus, bool query, Plan* plan) {
+    if (dtype < GEMM_I8 || dtype > GEMM_F32) return GEMM_ERR_INVALID_ARG;
+    if (layout != GEMM_LAYOUT_RR && layout != GEMM_LAYOUT_RC) return GEMM_ERR_INVALID_ARG;
+    if (variant != GEMM_VARIANT_REG && variant != GEMM_VARIANT_DIRECT) return GEMM_ERR_INVALID_ARG;
+    if (stages < 1 || stages > pg::kMaxStages) return GEMM_ERR_INVALID_ARG;
+    if (tile < GEMM_TILE_AUTO || tile >= pg::TILE_COUNT) return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+
+    const bool has_c = M > 0 && N > 0;
+    const bool reads_a = M > 0 && K > 0 && N > 0;
+    const bool reads_b = N > 0 && K > 0 && M > 0;
+    // A query may leave pointers NULL: then only their leading dimensions are checked.
+    if (reads_a && ((A == nullptr && !query) || lda < K)) return GEMM_ERR_INVALID_ARG;
+    if (reads_b && ((B == nullptr && !query) || ldb < (layout == GEMM_LAYOUT_RR ? N : K)))
+        return GEMM_ERR_INVALID_ARG;
+    if (has_c && ((C == nullptr && !query) || ldc < N)) return GEMM_ERR_INVALID_ARG;
+    if (lda < 0 || ldb < 0 || ldc < 0) return GEMM_ERR_INVALID_ARG;
+
+    const int sz = pg::in_size(dtype), osz = pg::out_size(dtype), epc = pg::epc(dtype);
+    if (reads_a && (!aligned16(A) || (lda * sz) % 16 != 0)) return GEMM_ERR_ALIGNMENT;
+    if (reads_b && (!aligned16(B) || (ldb * sz) % 16 != 0)) return GEMM_ERR_ALIGNMENT;
+    if (has_c && (!aligned16(C) || ldc % 4 != 0)) return GEMM_ERR_ALIGNMENT;
+    if (K % epc != 0) return GEMM_ERR_ALIGNMENT;
+    if (layout == GEMM_LAYOUT_RR && N % epc != 0) return GEMM_ERR_ALIGNMENT;
+    if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
+
+    // Tile class: the largest whose grid still gives every CU a workgroup.
+    int tc = tile;
+    if (tc == GEMM_TILE_AUTO) {
+        tc = pg::TILE_T;
+        const int order[3] = {pg::TILE_L, pg::TILE_M, pg::TILE_T};
+        for (int i = 0; i < 3; ++i) {
+            const pg::TileShape ts = pg::tile_shape(order[i]);
+            if (!instance_exists(layout, order[i])) continue;
+            if (ceil_div(M, ts.bm) * ceil_div(N, ts.bn) >= num_cus) { tc = order[i]; break; }
+        }
+    }
+    if (!instance_exists(layout, tc)) return GEMM_ERR_UNSUPPORTED;
+    if (!pg::instance_fits(dtype, tc, stages, variant)) return GEMM_ERR_UNSUPPORTED;
+
+    const pg::TileShape ts = pg::tile_shape(tc);
+    const int bk = pg::block_k(dtype, tc, stages);
+    // 32-bit buffer offsets: one workgroup's operand rows (and, for a
+    // row-major B, the whole K extent) must stay below 2^31 bytes.
+    const int64_t lim = (int64_t)1 << 31;
+    if ((int64_t)ts.bm * lda * sz >= lim || K * (int64_t)sz >= lim) return GEMM_ERR_UNSUPPORTED;
+    if (layout == GEMM_LAYOUT_RC && (int64_t)ts.bn * ldb * sz >= lim) return GEMM_ERR_UNSUPPORTED;
+    if (layout == GEMM_LAYOUT_RR && (K + bk) * ldb * (int64_t)sz >= lim) return GEMM_ERR_UNSUPPORTED;
+
+    const int64_t tm = has_c ? ceil_div(M, ts.bm) : 0, tn = has_c ? ceil_div(N, ts.bn) : 0;
+    if (tm * tn > INT_MAX) return GEMM_ERR_UNSUPPORTED;
+
+    gemm_config_info_t& in = plan->info;
+    memset(&in, 0, sizeof in);
+    in.tile = tc;
+    in.block_m = ts.bm;
+    in.block_n = ts.bn;
+    in.block_k = bk;
+    in.waves_m = ts.wm;
+    in.waves_n = ts.wn;
+    in.threads = pg::threads(tc);
+    in.lds_slots = pg::lds_slots(variant, stages);
+    in.reg_sets = pg::reg_sets(variant, stages);
+    in.tiles_in_flight = pg::tiles_in_flight(variant, stages);
+    in.lds_bytes = pg::lds_bytes(dtype, tc, stages, variant);
+    in.loads_per_tile = pg::loads_a(dtype, tc, stages) + pg::loads_b(dtype, tc, stages);
+    in.grid = tm * tn;
+    in.k_tiles = ceil_div(K, bk);
+    in.k_tail = (int32_t)(K % bk);
+    plan->tile = tc;
+    plan->tiles_m = tm;
+    plan->tiles_n = tn;
+    (void)osz;
+    return GEMM_OK;
+}
+
+struct Registry {
+    const void* fn[4][2][pg::TILE_COUNT][pg::kMaxStages + 1][2];
+    Registry() {
+        memset(fn, 0, sizeof fn);
+        const pg::KernelEntry* (*parts[4])(int*) = {pg::kernels_i8, pg::kernels_f16, pg::kernels_bf16,
+                                                    pg::kernels_f32};
+        for (int p = 0; p < 4; ++p) {
+            int n = 0;
+            const pg::KernelEntry* t = parts[p](&n);
+            for (int i = 0; i < n; ++i)
+                fn[t[i].dtype][t[i].layout][t[i].tile][t[i].stages][t[i].variant] = t[i].func;
+        }
+    }
+};
+
+const Registry& registry() {
+    static const Registry r;
+    return r;
+}
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return GEMM_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_create(gemm_handle_t* out, int device) {
+    if (out == nullptr || device < 0) return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return hip_fail(e);
+    if (device >= count) return hip_fail(hipErrorInvalidDevice);
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e);
+    gemm_handle_s* h = new (std::nothrow) gemm_handle_s;
+    if (h == nullptr) return GEMM_ERR_INVALID_ARG;
+    h->device = device;
+    h->num_cus = cus > 0 ? cus : kDefaultCus;
+    h->tile_override = GEMM_TILE_AUTO;
+    *out = h;
+    return GEMM_OK;
+}
+
+int gemm_destroy(gemm_handle_t h) {
+    delete h;
+    return GEMM_OK;
+}
+
+int gemm_set_tile(gemm_handle_t h, int tile) {
+    if (h == nullptr || tile < GEMM_TILE_AUTO || tile >= pg::TILE_COUNT) return GEMM_ERR_INVALID_ARG;
+    h->tile_override = tile;
+    return GEMM_OK;
+}
+
+int gemm_query(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
+               int tile, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+               int64_t ldc, gemm_config_info_t* info) {
+    if (info == nullptr) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, A, lda, B, ldb, C, ldc,
+                       kDefaultCus, true, &plan);
+    if (rc == GEMM_OK) *info = plan.info;
+    return rc;
+}
+
+int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+             int variant, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+             int64_t ldc, void* stream) {
+    if (h == nullptr) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, A, lda, B, ldb, C,
+                       ldc, h->num_cus, false, &plan);
+    if (rc != GEMM_OK) return rc;
+    if (plan.info.grid == 0) return GEMM_OK;
+
+    const void* fn = registry().fn[dtype][layout][plan.tile][stages][variant];
+    if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;
+
+    pg::GemmArgs args;
+    args.A = A;
+    args.B = B;
+    args.C = C;
+    args.lda = lda;
+    args.ldb = ldb;
+    args.ldc = ldc;
+    args.M = (int32_t)M;
+    args.N = (int32_t)N;
+    args.K = (int32_t)K;
+    args.tiles_m = (int32_t)plan.tiles_m;
+    args.tiles_n = (int32_t)plan.tiles_n;
+    args.pad = 0;
+
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess) return hip_fail(e);
+    void* kargs[] = {&args};
+    e = hipLaunchKernel(fn, dim3((unsigned)plan.info.grid), dim3((unsigned)plan.info.threads), kargs, 0,
+                        (hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (cur != h->device) hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e);
+    return GEMM_OK;
+}
+
+const char* gemm_status_string(int status) {
+    switch (status) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid argument";
+    case GEMM_ERR_ALIGNMENT: return "GEMM_ERR_ALIGNMENT: pointer, leading dimension or K not 16-byte aligned";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: no kernel instance for this configuration";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int gemm_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

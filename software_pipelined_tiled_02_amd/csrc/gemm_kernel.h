@@ -1,0 +1,508 @@
+// gemm_kernel.h -- the pipelined tiled GEMM kernel for gfx950 (device code).
+//
+// C = A * B over BM x BN x BK tiles.  The K loop is split into prologue,
+// main loop and drain so that the global->LDS copy of later K-tiles
+// overlaps the MFMA work on the current one ("CUDA Kernel Study:
+// Pipelining", Case 1 and Case 2; "pipeline-gpu-kernel", step 3).
+//
+// Two load paths (the pages' ping-pong vs cp.async contrast, Key
+// Differences):
+//  * DIRECT: buffer loads with the LDS bit set (LDS-DMA): each lane's 16
+//    bytes go from memory straight into the LDS slot, no VGPR in between.
+//    An LDS ring of STAGES slots; the prologue issues STAGES-1 tiles, each
+//    main-loop iteration waits with `s_waitcnt vmcnt(n)` until the oldest
+//    tile has landed (vmcnt counts this wave's outstanding loads, which
+//    retire in order -- the analogue of cp.async.wait_group), crosses one
+//    barrier, refills the slot every wave finished reading in the previous
+//    iteration, and multiplies the landed tile.  STAGES = 1 is the serial
+//    load / sync / compute / sync loop of the README's Background section.
+//  * REG: buffer loads into VGPR staging sets, then ds_write_b128 into one
+//    of two LDS slots (ping-pong).  max(1, STAGES-1) staging sets keep that
+//    many tiles in flight in registers; STAGES = 1 is the skill's
+//    register-only prefetch into a single LDS buffer (two barriers per
+//    iteration), STAGES >= 2 use one barrier per iteration.
+// Both paths put a tile in LDS in the same swizzled layout and run the same
+// MFMA sequence, so every (STAGES, variant) pair gives bit-identical C.
+//
+// MFMA mapping.  Both operands are read from LDS as one 16-byte chunk per
+// lane: lane l takes row (l % 32) of a 32-row fragment and chunk
+// (2*step + l/32) of the K-tile.  The B-side fragment is fed as the MFMA's
+// first operand and the A-side fragment as its second, so the 32x32 result
+// block is C^T and each lane ends up holding four consecutive columns of
+// one row of C -- which the epilogue stores as one vector per lane.
+// Any k order inside an MFMA is fine as long as both operands use the same
+// one, which they do by construction.
+//
+// Edges.  Rows past M (or N) and K-columns past K are loaded as zeros: the
+// lane's buffer offset is replaced by one beyond the buffer's range, and an
+// out-of-range buffer load returns 0 (also into LDS).  Stores are masked.
+#ifndef PIPEGEMM_GEMM_KERNEL_H
+#define PIPEGEMM_GEMM_KERNEL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernel_args.h"
+#include "tile_layout.h"
+
+namespace pg {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define PG_LDS __attribute__((address_space(3)))
+
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format,
+// no swizzle, no stride).
+constexpr int kRsrcWord3 = 0x00020000;
+// A buffer offset no valid element reaches: loads from it return zero.
+constexpr uint32_t kOob = 0x80000000u;
+
+template <int DT> struct AccT { typedef f32x16 type; };
+template <> struct AccT<DT_I8> { typedef i32x16 type; };
+
+// One 32x32 MFMA block step: acc += X * Y over the k values held in one
+// 16-byte chunk per lane of each operand.
+template <int DT>
+__device__ __forceinline__ typename AccT<DT>::type mfma_chunk(i32x4 x, i32x4 y, typename AccT<DT>::type c) {
+    if constexpr (DT == DT_BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    } else if constexpr (DT == DT_F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x),
+                                                      __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+    } else if constexpr (DT == DT_I8) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(x, y, c, 0, 0, 0);
+    } else {
+        // fp32: k = 2 per instruction, element s of each lane's chunk.  (Whole
+        // vectors are bit-cast, then indexed: a bit-cast of one vector
+        // element would read element 0.)
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 xf = __builtin_bit_cast(f32x4, x), yf = __builtin_bit_cast(f32x4, y);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[0], yf[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[1], yf[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[2], yf[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[3], yf[3], c, 0, 0, 0);
+        return c;
+    }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits
+// 6:4, lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier that also drains this wave's LDS accesses first.
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int DT, int LAYOUT, int TC, int STAGES, int VARIANT>
+struct Gemm {
+    static constexpr TileShape TS = tile_shape(TC);
+    static constexpr int BM = TS.bm, BN = TS.bn, WM = TS.wm, WN = TS.wn;
+    static constexpr int T = WM * WN * 64;
+    static constexpr int SZ = in_size(DT), OSZ = out_size(DT), EPC = epc(DT);
+    static constexpr int CPR = cpr_k(TC, STAGES);          // chunks per K-contiguous row
+    static constexpr int BK = CPR * EPC;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int KSTEPS = CPR / 2;                  // two chunks per MFMA step
+    static constexpr int LA = loads_a(DT, TC, STAGES), LB = loads_b(DT, TC, STAGES);
+    static constexpr int LPT = LA + LB;
+    static constexpr int A_BYTES = BM * CPR * kChunk;
+    static constexpr int B_BYTES = BN * BK * SZ;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int SLOTS = lds_slots(VARIANT, STAGES);
+    static constexpr int RSETS = reg_sets(VARIANT, STAGES);
+    static constexpr int LDS = SLOT * SLOTS;
+    static constexpr bool RR = (LAYOUT == LAYOUT_RR);
+    static constexpr int CPR_BRR = BN * SZ / kChunk;       // chunks per row of a K x N B tile
+    typedef typename AccT<DT>::type acc_t;
+
+    static_assert(instance_fits(DT, TC, STAGES, VARIANT), "instance over budget");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static_assert(T % CPR == 0, "loader rows");
+    static_assert(!RR || (BK * CPR_BRR) % T == 0, "RR loader");
+    static_assert(LPT * (STAGES > 1 ? STAGES - 1 : 1) < 64, "vmcnt range");
+
+    // ---- per-lane state --------------------------------------------------
+    struct State {
+        __amdgpu_buffer_rsrc_t ra, rb;
+        uint32_t offa[LA], offb[LB];   // byte offsets at K-tile 0 (kOob if the row is outside)
+        uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
+        uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
+        uint32_t kb_step;              // byte advance of the B offset per K-tile
+        int K, nt;
+        int tid, wave, wm, wn;
+    };
+
+    __device__ static __forceinline__ void lds_dma(const State& s, bool is_a, uint8_t PG_LDS* dst, uint32_t off) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? s.ra : s.rb, (void PG_LDS*)dst, 16, off, 0, 0, 0);
+    }
+
+    // Byte offset of this lane's j-th chunk of K-tile kt, or kOob.
+    __device__ static __forceinline__ uint32_t off_a(const State& s, int j, int kt) {
+        uint32_t off = s.offa[j] + (uint32_t)kt * (uint32_t)(BK * SZ);
+        if ((kt + 1) * BK > s.K && s.kca[j] + (uint32_t)kt * BK >= (uint32_t)s.K) off = kOob;
+        return off;
+    }
+    __device__ static __forceinline__ uint32_t off_b(const State& s, int j, int kt) {
+        uint32_t off = s.offb[j] + (uint32_t)kt * s.kb_step;
+        if ((kt + 1) * BK > s.K && s.kcb[j] + (uint32_t)kt * BK >= (uint32_t)s.K) off = kOob;
+        return off;
+    }
+
+    // DIRECT: issue every chunk of K-tile kt into LDS slot `slot`.  Chunk j
+    // of wave w lands at physical chunk j*T + 64*w + lane, the order LDS-DMA
+    // writes in; the lane's source chunk is the logical one stored there.
+    __device__ static __forceinline__ void issue_direct(const State& s, uint8_t PG_LDS* smem, int kt, int slot) {
+        uint8_t PG_LDS* base = smem + slot * SLOT;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
+#pragma unroll
+        for (int j = 0; j < LB; ++j)
+            lds_dma(s, false, base + A_BYTES + (j * T + 64 * s.wave) * kChunk, off_b(s, j, kt));
+    }
+
+    // REG: load K-tile kt into a VGPR staging set / store a set into a slot.
+    __device__ static __forceinline__ void gload(const State& s, i32x4 (&r)[LPT], int kt) {
+#pragma unroll
+        for (int j = 0; j < LA; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
+#pragma unroll
+        for (int j = 0; j < LB; ++j) r[LA + j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j, kt), 0, 0);
+    }
+    __device__ static __forceinline__ void swrite(const State& s, uint8_t PG_LDS* smem, const i32x4 (&r)[LPT], int slot) {
+        i32x4 PG_LDS* base = (i32x4 PG_LDS*)(smem + slot * SLOT);
+#pragma unroll
+        for (int j = 0; j < LA; ++j) base[j * T + s.tid] = r[j];
+#pragma unroll
+        for (int j = 0; j < LB; ++j) base[A_BYTES / kChunk + j * T + s.tid] = r[LA + j];
+    }
+
+    // RR B fragment: gather the EPC k-consecutive elements of one column.
+    __device__ static __forceinline__ i32x4 gather_b_rr(const uint8_t PG_LDS* bt, int n, int k0) {
+        i32x4 v;
+        if constexpr (SZ == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = *(const int PG_LDS*)(bt + ((k0 + e) * BN + n) * 4);
+        } else if constexpr (SZ == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t lo = *(const uint16_t PG_LDS*)(bt + ((k0 + 2 * e) * BN + n) * 2);
+                uint32_t hi = *(const uint16_t PG_LDS*)(bt + ((k0 + 2 * e + 1) * BN + n) * 2);
+                v[e] = (int)(lo | (hi << 16));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    w |= (uint32_t)(*(const uint8_t PG_LDS*)(bt + (k0 + 4 * e + b) * BN + n)) << (8 * b);
+                v[e] = (int)w;
+            }
+        }
+        return v;
+    }
+
+    // Operand fragments of MFMA step `st` of the K-tile at (as, bs).
+    __device__ static __forceinline__ void read_frags(const State& s, const uint8_t PG_LDS* as,
+                                                      const uint8_t PG_LDS* bs, int st,
+                                                      i32x4 (&y)[FM], i32x4 (&x)[FN]) {
+        const int lane = s.tid & 63;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            y[fm] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + fm * 32) * CPR * kChunk + s.rd[st]);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            if constexpr (RR)
+                x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
+            else
+                x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
+        }
+    }
+
+    static constexpr int MFMA_PER_BLOCK = (DT == DT_F32) ? 4 : 1;
+
+    // Multiply the K-tile held in `slot` into the accumulators.  The
+    // fragments of step st+1 are read while the MFMAs of step st run (a
+    // two-deep register pipeline inside the tile), and the scheduler is
+    // asked to alternate one MFMA with one LDS read so the reads hide under
+    // matrix-core time instead of stalling before each MFMA group.
+    __device__ static __forceinline__ void compute(const State& s, const uint8_t PG_LDS* smem, int slot,
+                                                   acc_t (&acc)[FM][FN]) {
+        const uint8_t PG_LDS* as = smem + slot * SLOT;
+        const uint8_t PG_LDS* bs = as + A_BYTES;
+        i32x4 y[2][FM], x[2][FN];
+        read_frags(s, as, bs, 0, y[0], x[0]);
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            if (st + 1 < KSTEPS) read_frags(s, as, bs, st + 1, y[(st + 1) & 1], x[(st + 1) & 1]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = mfma_chunk<DT>(x[st & 1][fn], y[st & 1][fm], acc[fm][fn]);
+        }
+        if constexpr (!RR) {
+            constexpr int NR = FM + FN;                       // LDS reads per step
+            constexpr int NM = FM * FN * MFMA_PER_BLOCK;      // MFMAs per step
+            constexpr int PAIRS = NR < NM ? NR : NM;
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // step-0 reads
+#pragma unroll
+            for (int st = 0; st + 1 < KSTEPS; ++st) {
+#pragma unroll
+                for (int i = 0; i < PAIRS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                if constexpr (NR > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NR - PAIRS, 0);
+                if constexpr (NM > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        }
+    }
+
+    // Tiles issued after kt that may still be in flight when kt is needed.
+    __device__ static __forceinline__ void wait_tile_direct(int ahead) {
+        if constexpr (STAGES >= 2) {
+            if (ahead >= STAGES - 2) { wait_vmcnt<LPT * (STAGES - 2)>(); return; }
+        }
+        if constexpr (STAGES >= 4) { if (ahead == 1) { wait_vmcnt<LPT>(); return; } }
+        wait_vmcnt<0>();
+    }
+
+    __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
+        State s;
+        s.tid = threadIdx.x;
+        s.wave = __builtin_amdgcn_readfirstlane(s.tid >> 6);
+        s.wm = s.wave / WN;
+        s.wn = s.wave % WN;
+        const int lane = s.tid & 63;
+
+        // Workgroup -> C tile.  Workgroups are handed to the 8 XCDs round
+        // robin; regroup so that each XCD gets a contiguous run of tiles, and
+        // order the runs in bands of kGroupM tile-rows so that the tiles one
+        // XCD holds at a time share A rows and B columns in its L2.
+        int w = blockIdx.x;
+        const int G = gridDim.x;
+        if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+        constexpr int kGroupM = 4;
+        const int band = kGroupM * args.tiles_n;
+        const int g = w / band;
+        const int first_m = g * kGroupM;
+        const int gm = min(args.tiles_m - first_m, kGroupM);
+        const int r_in = w - g * band;
+        const int tm = first_m + r_in % gm;
+        const int tn = r_in / gm;
+        const int m0 = tm * BM, n0 = tn * BN;
+
+        s.K = args.K;
+        s.nt = (args.K + BK - 1) / BK;
+        const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
+        const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
+                              : (const uint8_t*)args.B + (int64_t)n0 * args.ldb * SZ;
+        s.ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, 0x7fffffff, kRsrcWord3);
+        s.rb = __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, 0x7fffffff, kRsrcWord3);
+        const uint32_t lda_b = (uint32_t)(args.lda * SZ), ldb_b = (uint32_t)(args.ldb * SZ);
+
+#pragma unroll
+        for (int j = 0; j < LA; ++j) {
+            const int p = j * T + s.tid;
+            const int r = logical_row(CPR, p), c = logical_chunk(CPR, p);
+            s.offa[j] = (m0 + r < args.M) ? (uint32_t)r * lda_b + (uint32_t)(c * EPC * SZ) : kOob;
+            s.kca[j] = (uint32_t)(c * EPC);
+        }
+        if constexpr (RR) {
+            // B tile is BK rows (k) of BN elements (n), unswizzled.
+#pragma unroll
+            for (int j = 0; j < LB; ++j) {
+                const int p = j * T + s.tid;
+                const int r = p / CPR_BRR, c = p % CPR_BRR;
+                s.offb[j] = (n0 + c * EPC < args.N) ? (uint32_t)r * ldb_b + (uint32_t)(c * EPC * SZ) : kOob;
+                s.kcb[j] = (uint32_t)r;
+            }
+            s.kb_step = (uint32_t)BK * ldb_b;
+        } else {
+#pragma unroll
+            for (int j = 0; j < LB; ++j) {
+                const int p = j * T + s.tid;
+                const int r = logical_row(CPR, p), c = logical_chunk(CPR, p);
+                s.offb[j] = (n0 + r < args.N) ? (uint32_t)r * ldb_b + (uint32_t)(c * EPC * SZ) : kOob;
+                s.kcb[j] = (uint32_t)(c * EPC);
+            }
+            s.kb_step = (uint32_t)(BK * SZ);
+        }
+#pragma unroll
+        for (int st = 0; st < KSTEPS; ++st) {
+            const int t = lane & 31, h = lane >> 5;
+            s.rd[st] = (uint32_t)(t * CPR + ((2 * st + h) ^ swz(CPR, t))) * kChunk;
+        }
+
+        acc_t acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0;
+
+        const int nt = s.nt;
+        if constexpr (VARIANT == VAR_DIRECT) {
+            if constexpr (STAGES == 1) {
+                for (int kt = 0; kt < nt; ++kt) {
+                    issue_direct(s, smem, kt, 0);
+                    wait_vmcnt<0>();
+                    block_sync();
+                    compute(s, smem, 0, acc);
+                    block_sync();
+                }
+            } else {
+                // prologue: fill STAGES-1 slots
+#pragma unroll
+                for (int t = 0; t < STAGES - 1; ++t)
+                    if (t < nt) issue_direct(s, smem, t, t);
+                int slot = 0;
+                for (int kt = 0; kt < nt; ++kt) {
+                    wait_tile_direct(nt - 1 - kt);   // tile kt landed (this wave's part)
+                    block_sync();                    // ...every wave's part; slot kt-1 free
+                    if (kt + STAGES - 1 < nt)
+                        issue_direct(s, smem, kt + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
+                    compute(s, smem, slot, acc);
+                    slot = (slot + 1 == STAGES) ? 0 : slot + 1;
+                }
+            }
+        } else {
+            i32x4 regs[RSETS][LPT];
+            if constexpr (STAGES == 1) {
+                if (nt > 0) {
+                    gload(s, regs[0], 0);
+                    swrite(s, smem, regs[0], 0);
+                }
+                block_sync();
+                if (1 < nt) gload(s, regs[0], 1);
+                for (int kt = 0; kt < nt; ++kt) {
+                    compute(s, smem, 0, acc);
+                    if (kt + 1 < nt) {
+                        block_sync();                 // every wave done reading the slot
+                        swrite(s, smem, regs[0], 0);  // tile kt+1
+                        block_sync();
+                        if (kt + 2 < nt) gload(s, regs[0], kt + 2);
+                    }
+                }
+            } else {
+                constexpr int R = RSETS;
+#pragma unroll
+                for (int t = 0; t < R; ++t)
+                    if (t < nt) gload(s, regs[t], t);
+                if (nt > 0) swrite(s, smem, regs[0], 0);
+                if (R < nt) gload(s, regs[0], R);
+                block_sync();
+                for (int kb = 0; kb < nt; kb += R) {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const int kt = kb + i;
+                        if (kt < nt) {
+                            compute(s, smem, kt & 1, acc);
+                            if (kt + 1 < nt) {
+                                // tile kt+1 sits in set (kt+1) % R == (i+1) % R
+                                swrite(s, smem, regs[(i + 1) % R], (kt + 1) & 1);
+                                if (kt + 1 + R < nt) gload(s, regs[(i + 1) % R], kt + 1 + R);
+                                block_sync();
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        // Epilogue: lane holds C[m][n .. n+3] of each 32x32 block.
+        const int t = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = m0 + s.wm * WTM + fm * 32 + t;
+            if (m >= args.M) continue;
+            uint8_t* crow = (uint8_t*)args.C + (int64_t)m * args.ldc * OSZ;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = n0 + s.wn * WTN + fn * 32 + 8 * q + 4 * h;
+                    store4(crow, n, args.N, acc[fm][fn], q);
+                }
+            }
+        }
+    }
+
+    __device__ static __forceinline__ void store4(uint8_t* crow, int n, int N, const acc_t& a, int q) {
+        if constexpr (DT == DT_I8 || DT == DT_F32) {
+            const i32x16 ai = __builtin_bit_cast(i32x16, a);   // whole-vector cast
+            i32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = ai[4 * q + e];
+            if (n + 4 <= N) {
+                *(i32x4*)(crow + (int64_t)n * 4) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) *(int*)(crow + (int64_t)(n + e) * 4) = v[e];
+            }
+        } else {
+            uint16_t hv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (DT == DT_BF16) hv[e] = f32_to_bf16_rne(a[4 * q + e]);
+                else hv[e] = __builtin_bit_cast(uint16_t, (_Float16)a[4 * q + e]);
+            }
+            if (n + 4 <= N) {
+                i32x2 v;
+                v[0] = (int)(hv[0] | ((uint32_t)hv[1] << 16));
+                v[1] = (int)(hv[2] | ((uint32_t)hv[3] << 16));
+                *(i32x2*)(crow + (int64_t)n * 2) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) *(uint16_t*)(crow + (int64_t)(n + e) * 2) = hv[e];
+            }
+        }
+    }
+};
+
+template <int DT, int LAYOUT, int TC, int STAGES, int VARIANT>
+__global__ void __launch_bounds__(threads(TC), 1)
+pipegemm_kernel(GemmArgs args) {
+    typedef Gemm<DT, LAYOUT, TC, STAGES, VARIANT> G;
+    __shared__ __attribute__((aligned(16))) uint8_t smem_raw[G::LDS];
+    // Field-by-field copy: keeps every argument a uniform (scalar) value.
+    GemmArgs a;
+    a.A = args.A; a.B = args.B; a.C = args.C;
+    a.lda = args.lda; a.ldb = args.ldb; a.ldc = args.ldc;
+    a.M = args.M; a.N = args.N; a.K = args.K;
+    a.tiles_m = args.tiles_m; a.tiles_n = args.tiles_n; a.pad = 0;
+    G::run(a, (uint8_t PG_LDS*)smem_raw);
+}
+
+}  // namespace pg
+
+#endif

@@ -1,0 +1,43 @@
+// instances.h -- the kernel instances one translation unit compiles for one
+// input type: layout RC at every tile class, layout RR at the 128x128 and
+// 32x64 tiles, each at stages 1-4 and both load variants.
+#ifndef PIPEGEMM_INSTANCES_H
+#define PIPEGEMM_INSTANCES_H
+
+#include "gemm_kernel.h"
+
+namespace pg {
+
+template <int DT, int LAYOUT, int TC, int S, int V>
+inline KernelEntry entry() {
+    return KernelEntry{DT, LAYOUT, TC, S, V, (const void*)&pipegemm_kernel<DT, LAYOUT, TC, S, V>};
+}
+
+template <int DT, int LAYOUT, int TC>
+inline void add_tile(KernelEntry* t, int& n) {
+    t[n++] = entry<DT, LAYOUT, TC, 1, VAR_REG>();
+    t[n++] = entry<DT, LAYOUT, TC, 2, VAR_REG>();
+    t[n++] = entry<DT, LAYOUT, TC, 3, VAR_REG>();
+    t[n++] = entry<DT, LAYOUT, TC, 4, VAR_REG>();
+    t[n++] = entry<DT, LAYOUT, TC, 1, VAR_DIRECT>();
+    t[n++] = entry<DT, LAYOUT, TC, 2, VAR_DIRECT>();
+    t[n++] = entry<DT, LAYOUT, TC, 3, VAR_DIRECT>();
+    t[n++] = entry<DT, LAYOUT, TC, 4, VAR_DIRECT>();
+}
+
+constexpr int kInstancesPerDtype = 5 * 8;
+
+template <int DT>
+inline int fill_instances(KernelEntry* t) {
+    int n = 0;
+    add_tile<DT, LAYOUT_RC, TILE_L>(t, n);
+    add_tile<DT, LAYOUT_RC, TILE_M>(t, n);
+    add_tile<DT, LAYOUT_RC, TILE_T>(t, n);
+    add_tile<DT, LAYOUT_RR, TILE_M>(t, n);
+    add_tile<DT, LAYOUT_RR, TILE_T>(t, n);
+    return n;
+}
+
+}  // namespace pg
+
+#endif

@@ -1,0 +1,121 @@
+// tile_layout.h -- tile shapes, stage/K-tile choices and the LDS layout of a
+// pipelined GEMM tile.  Plain constexpr C++ with no HIP dependency: the
+// kernels, the host-side configuration code and a host test all include it,
+// so the three agree by construction.
+//
+// Background.  Software pipelining keeps the next K-tile's global->shared
+// copy in flight while the current tile is multiplied ("CUDA Kernel Study:
+// Pipelining", Background / Case 1 / Case 2).  The shared-memory cost is
+// slots x tile, and the tile must stay under the occupancy cliff set by the
+// per-block shared-memory budget ("pipeline-gpu-kernel", step 1).  On gfx950
+// the budget is the 160 KiB LDS of one CU; these kernels run one workgroup
+// per CU, so a workgroup may use all of it.
+//
+// LDS layout.  Every operand tile is a grid of 16-byte chunks: `rows` rows of
+// `cpr` chunks (cpr = chunks per row).  A tile is written row-major in chunk
+// order, lane-contiguous (one 16-byte chunk per lane per instruction), which
+// is the only order the direct-to-LDS load can produce.  Inside a row the
+// chunk a row's logical chunk c lives in is c ^ swz(row): an XOR swizzle that
+// costs no LDS bytes (padding would cost 1/cpr of the tile) and spreads the
+// 16-byte reads of 8 or 16 consecutive rows at one logical chunk over all
+// banks, whether the LDS serves 8 lanes x 16 B (32 banks) or 16 lanes x 16 B
+// (64 banks) per clock.  The padding/swizzling remedy for shared-memory bank
+// conflicts is the next step the pipelining study names (Detailed Analysis,
+// item 5).
+#ifndef PIPEGEMM_TILE_LAYOUT_H
+#define PIPEGEMM_TILE_LAYOUT_H
+
+#include <stdint.h>
+
+namespace pg {
+
+enum DType : int { DT_I8 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
+enum Layout : int { LAYOUT_RR = 0, LAYOUT_RC = 1 };
+enum Variant : int { VAR_REG = 0, VAR_DIRECT = 1 };
+enum TileClass : int { TILE_L = 0, TILE_M = 1, TILE_T = 2, TILE_COUNT = 3 };
+
+constexpr int kMaxStages = 4;
+constexpr int kLdsBudget = 160 * 1024;   // bytes of LDS per CU on gfx950
+constexpr int kChunk = 16;               // bytes per lane per load
+
+constexpr int in_size(int dt) { return dt == DT_I8 ? 1 : (dt == DT_F32 ? 4 : 2); }
+constexpr int out_size(int dt) { return dt == DT_I8 ? 4 : (dt == DT_F32 ? 4 : 2); }
+// elements per 16-byte chunk
+constexpr int epc(int dt) { return kChunk / in_size(dt); }
+
+// Workgroup tile and wave grid of each class.  Each wave owns a
+// (bm/wm) x (bn/wn) block of C made of 32x32 MFMA blocks.
+struct TileShape { int bm, bn, wm, wn; };
+constexpr TileShape tile_shape(int tc) {
+    return tc == TILE_L ? TileShape{256, 256, 2, 2}
+         : tc == TILE_M ? TileShape{128, 128, 2, 2}
+                        : TileShape{32, 64, 1, 2};
+}
+
+// Chunks per K-contiguous row of a K-tile.  The large tile halves its K-tile
+// at 3-4 stages so that the ring stays inside the LDS budget (the remedy the
+// skill gives for a buffer over the cliff: halve BK).
+constexpr int cpr_k(int tc, int stages) {
+    return tc == TILE_L ? (stages <= 2 ? 8 : 4) : tc == TILE_M ? 8 : 16;
+}
+constexpr int block_k(int dt, int tc, int stages) { return cpr_k(tc, stages) * epc(dt); }
+
+// LDS slots of the ring and register staging sets per variant:
+//  direct-to-LDS: `stages` slots, stages-1 tiles in flight, no staging set;
+//  register-staged: min(stages, 2) slots and max(1, stages-1) staging sets,
+//  each holding one tile in flight.
+constexpr int lds_slots(int variant, int stages) {
+    return variant == VAR_DIRECT ? stages : (stages < 2 ? stages : 2);
+}
+constexpr int reg_sets(int variant, int stages) {
+    return variant == VAR_DIRECT ? 0 : (stages > 1 ? stages - 1 : 1);
+}
+constexpr int tiles_in_flight(int variant, int stages) {
+    return variant == VAR_DIRECT ? stages - 1 : reg_sets(variant, stages);
+}
+
+// Bytes of one ring slot (A tile followed by B tile).
+constexpr int slot_bytes(int dt, int tc, int stages) {
+    return (tile_shape(tc).bm + tile_shape(tc).bn) * block_k(dt, tc, stages) * in_size(dt);
+}
+constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
+    return slot_bytes(dt, tc, stages) * lds_slots(variant, stages);
+}
+constexpr int threads(int tc) { return tile_shape(tc).wm * tile_shape(tc).wn * 64; }
+
+// 16-byte loads per lane per K-tile for each operand.
+constexpr int loads_a(int dt, int tc, int stages) {
+    return tile_shape(tc).bm * (block_k(dt, tc, stages) * in_size(dt) / kChunk) / threads(tc);
+}
+constexpr int loads_b(int dt, int tc, int stages) {
+    return tile_shape(tc).bn * (block_k(dt, tc, stages) * in_size(dt) / kChunk) / threads(tc);
+}
+
+// XOR swizzle of a K-contiguous row (see the header comment).  It depends
+// only on row % 32, so a fragment of 32 rows starting at a multiple of 32
+// has the same per-lane swizzle wherever it sits in the tile.
+constexpr int swz(int cpr, int row) {
+    return cpr >= 16 ? (row & 15)
+         : cpr == 8  ? ((row & 7) ^ ((row >> 3) & 3))
+         : cpr == 4  ? (((row >> 1) ^ (row >> 3)) & 3)
+                     : 0;
+}
+// Physical chunk index (within the tile) of logical (row, chunk).
+constexpr int phys_chunk(int cpr, int row, int chunk) { return row * cpr + (chunk ^ swz(cpr, row)); }
+// Logical chunk that physical chunk p holds (the inverse of the above).
+constexpr int logical_row(int cpr, int p) { return p / cpr; }
+constexpr int logical_chunk(int cpr, int p) { return (p % cpr) ^ swz(cpr, p / cpr); }
+
+// Budget check of one instance: LDS ring within the CU's LDS, and every
+// per-lane load count a whole number.
+constexpr bool instance_fits(int dt, int tc, int stages, int variant) {
+    return stages >= 1 && stages <= kMaxStages
+        && lds_bytes(dt, tc, stages, variant) <= kLdsBudget
+        && (tile_shape(tc).bm * cpr_k(tc, stages)) % threads(tc) == 0
+        && (tile_shape(tc).bn * cpr_k(tc, stages)) % threads(tc) == 0
+        && loads_a(dt, tc, stages) >= 1 && loads_b(dt, tc, stages) >= 1;
+}
+
+}  // namespace pg
+
+#endif

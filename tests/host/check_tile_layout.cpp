@@ -1,0 +1,66 @@
+// Host check of tile_layout.h (the header the kernels include):
+//  1. the XOR swizzle is a bijection inside every row, and logical_chunk()
+//     inverts phys_chunk();
+//  2. a fragment read -- lane l reads row (rb + l % 32) at chunk
+//     (c0 + l / 32), rb a multiple of 32 -- is free of LDS bank conflicts
+//     whether the LDS serves 8 lanes x 16 B per clock (32 banks of 4 B) or
+//     16 lanes x 16 B (64 banks): within each group of lanes served
+//     together, the 16-byte bank groups hit must all differ;
+//  3. without the swizzle the same read does conflict (so 2 is not vacuous).
+// Prints one line per chunks-per-row value; exits non-zero on failure.
+#include <cstdio>
+#include "tile_layout.h"
+
+using namespace pg;
+
+static int conflict_ways(int cpr, bool swizzled, int lanes_per_clock, int rb, int c0) {
+    int worst = 1;
+    for (int g0 = 0; g0 < 64; g0 += lanes_per_clock) {
+        int hits[64] = {0};
+        for (int l = g0; l < g0 + lanes_per_clock; ++l) {
+            const int row = rb + (l % 32), chunk = c0 + l / 32;
+            const int p = swizzled ? phys_chunk(cpr, row, chunk) : row * cpr + chunk;
+            const int bank_group = p % lanes_per_clock;
+            if (++hits[bank_group] > worst) worst = hits[bank_group];
+        }
+    }
+    return worst;
+}
+
+int main() {
+    int fail = 0;
+    const int cprs[] = {4, 8, 16, 32};
+    for (int cpr : cprs) {
+        for (int row = 0; row < 512; ++row) {
+            bool seen[64] = {false};
+            for (int c = 0; c < cpr; ++c) {
+                const int p = phys_chunk(cpr, row, c);
+                if (p < row * cpr || p >= (row + 1) * cpr || seen[p - row * cpr]) { ++fail; break; }
+                seen[p - row * cpr] = true;
+                if (logical_row(cpr, p) != row || logical_chunk(cpr, p) != c) ++fail;
+            }
+            if (swz(cpr, row) != swz(cpr, row % 32)) ++fail;  // depends on row % 32 only
+        }
+        int worst8 = 1, worst16 = 1, raw8 = 1, raw16 = 1;
+        for (int rb = 0; rb < 256; rb += 32)
+            for (int c0 = 0; c0 + 1 < cpr; c0 += 2) {
+                int w;
+                if ((w = conflict_ways(cpr, true, 8, rb, c0)) > worst8) worst8 = w;
+                if ((w = conflict_ways(cpr, true, 16, rb, c0)) > worst16) worst16 = w;
+                if ((w = conflict_ways(cpr, false, 8, rb, c0)) > raw8) raw8 = w;
+                if ((w = conflict_ways(cpr, false, 16, rb, c0)) > raw16) raw16 = w;
+            }
+        std::printf("cpr=%d swizzled: %d-way (8 lanes/clk) %d-way (16 lanes/clk); unswizzled: %d-way %d-way\n",
+                    cpr, worst8, worst16, raw8, raw16);
+        if (worst8 != 1 || worst16 != 1) ++fail;
+        if (raw8 == 1 && raw16 == 1) ++fail;
+    }
+    // every instance the library builds fits the LDS budget
+    for (int dt = 0; dt < 4; ++dt)
+        for (int tc = 0; tc < TILE_COUNT; ++tc)
+            for (int s = 1; s <= kMaxStages; ++s)
+                for (int v = 0; v < 2; ++v)
+                    if (!instance_fits(dt, tc, s, v)) { std::printf("over budget %d %d %d %d\n", dt, tc, s, v); ++fail; }
+    std::printf(fail ? "FAIL (%d)\n" : "OK\n", fail);
+    return fail ? 1 : 0;
+}
