@@ -9,12 +9,11 @@
 // Differences):
 //  * DIRECT: buffer loads with the LDS bit set (LDS-DMA): each lane's 16
 //    bytes go from memory straight into the LDS slot, no VGPR in between.
-//    An LDS ring of STAGES slots; the prologue issues STAGES-1 tiles, each
-//    main-loop iteration waits with `s_waitcnt vmcnt(n)` until the oldest
+//    An LDS ring of STAGES slots; the prologue fills every slot, and at each
+//    tile boundary the wave waits with `s_waitcnt vmcnt(n)` until the next
 //    tile has landed (vmcnt counts this wave's outstanding loads, which
 //    retire in order -- the analogue of cp.async.wait_group), crosses one
-//    barrier, refills the slot every wave finished reading in the previous
-//    iteration, and multiplies the landed tile.  STAGES = 1 is the serial
+//    barrier, and refills the slot every wave has just finished reading.  STAGES = 1 is the serial
 //    load / sync / compute / sync loop of the README's Background section.
 //  * REG: buffer loads into VGPR staging sets, then ds_write_b128 into one
 //    of two LDS slots (ping-pong).  max(1, STAGES-1) staging sets keep that
@@ -144,6 +143,7 @@ struct Gemm {
     static_assert(T % CPR == 0, "loader rows");
     static_assert(!RR || (BK * CPR_BRR) % T == 0, "RR loader");
     static_assert(LPT * (STAGES > 1 ? STAGES - 1 : 1) < 64, "vmcnt range");
+    static_assert(KSTEPS >= 2, "at least two MFMA steps per K-tile");
 
     // ---- per-lane state --------------------------------------------------
     struct State {
@@ -172,25 +172,33 @@ struct Gemm {
         return off;
     }
 
-    // DIRECT: issue every chunk of K-tile kt into LDS slot `slot`.  Chunk j
-    // of wave w lands at physical chunk j*T + 64*w + lane, the order LDS-DMA
+    // DIRECT: issue chunks J0 .. J1-1 of K-tile kt into LDS slot `slot`
+    // (chunks 0 .. LA-1 are the A tile, LA .. LPT-1 the B tile).  Chunk j of
+    // wave w lands at physical chunk j*T + 64*w + lane, the order LDS-DMA
     // writes in; the lane's source chunk is the logical one stored there.
+    template <int J0, int J1>
     __device__ static __forceinline__ void issue_direct(const State& s, uint8_t PG_LDS* smem, int kt, int slot) {
         uint8_t PG_LDS* base = smem + slot * SLOT;
 #pragma unroll
-        for (int j = 0; j < LA; ++j)
-            lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
-#pragma unroll
-        for (int j = 0; j < LB; ++j)
-            lds_dma(s, false, base + A_BYTES + (j * T + 64 * s.wave) * kChunk, off_b(s, j, kt));
+        for (int j = J0; j < J1; ++j) {
+            if (j < LA)
+                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
+            else
+                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, off_b(s, j - LA, kt));
+        }
     }
 
-    // REG: load K-tile kt into a VGPR staging set / store a set into a slot.
+    // REG: load chunks J0 .. J1-1 of K-tile kt into a VGPR staging set /
+    // store a whole set into a slot.
+    template <int J0, int J1>
     __device__ static __forceinline__ void gload(const State& s, i32x4 (&r)[LPT], int kt) {
 #pragma unroll
-        for (int j = 0; j < LA; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
-#pragma unroll
-        for (int j = 0; j < LB; ++j) r[LA + j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j, kt), 0, 0);
+        for (int j = J0; j < J1; ++j) {
+            if (j < LA)
+                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
+            else
+                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j - LA, kt), 0, 0);
+        }
     }
     __device__ static __forceinline__ void swrite(const State& s, uint8_t PG_LDS* smem, const i32x4 (&r)[LPT], int slot) {
         i32x4 PG_LDS* base = (i32x4 PG_LDS*)(smem + slot * SLOT);
@@ -226,71 +234,95 @@ struct Gemm {
         return v;
     }
 
-    // Operand fragments of MFMA step `st` of the K-tile at (as, bs).
-    __device__ static __forceinline__ void read_frags(const State& s, const uint8_t PG_LDS* as,
-                                                      const uint8_t PG_LDS* bs, int st,
-                                                      i32x4 (&y)[FM], i32x4 (&x)[FN]) {
+    // Operand fragments of one MFMA step: FM A-side and FN B-side chunks.
+    struct Frags {
+        i32x4 y[FM];
+        i32x4 x[FN];
+    };
+
+    __device__ static __forceinline__ const uint8_t PG_LDS* slot_ptr(const uint8_t PG_LDS* smem, int slot) {
+        return smem + slot * SLOT;
+    }
+
+    // Fragments of MFMA step `st` of the K-tile held in `slot`.
+    __device__ static __forceinline__ void read_frags(const State& s, const uint8_t PG_LDS* smem, int slot,
+                                                      int st, Frags& f) {
+        const uint8_t PG_LDS* as = slot_ptr(smem, slot);
+        const uint8_t PG_LDS* bs = as + A_BYTES;
         const int lane = s.tid & 63;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            y[fm] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + fm * 32) * CPR * kChunk + s.rd[st]);
+            f.y[fm] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + fm * 32) * CPR * kChunk + s.rd[st]);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             if constexpr (RR)
-                x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
+                f.x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
             else
-                x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
+                f.x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
         }
+    }
+
+    __device__ static __forceinline__ void mfma_step(const Frags& f, acc_t (&acc)[FM][FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = mfma_chunk<DT>(f.x[fn], f.y[fm], acc[fm][fn]);
     }
 
     static constexpr int MFMA_PER_BLOCK = (DT == DT_F32) ? 4 : 1;
+    static constexpr int NR = RR ? FM + FN * EPC : FM + FN;   // LDS read instructions per step
+    static constexpr int NM = FM * FN * MFMA_PER_BLOCK;        // MFMA instructions per step
 
-    // Multiply the K-tile held in `slot` into the accumulators.  The
-    // fragments of step st+1 are read while the MFMAs of step st run (a
-    // two-deep register pipeline inside the tile), and the scheduler is
-    // asked to alternate one MFMA with one LDS read so the reads hide under
-    // matrix-core time instead of stalling before each MFMA group.
-    __device__ static __forceinline__ void compute(const State& s, const uint8_t PG_LDS* smem, int slot,
-                                                   acc_t (&acc)[FM][FN]) {
-        const uint8_t PG_LDS* as = smem + slot * SLOT;
-        const uint8_t PG_LDS* bs = as + A_BYTES;
-        i32x4 y[2][FM], x[2][FN];
-        read_frags(s, as, bs, 0, y[0], x[0]);
-#pragma unroll
-        for (int st = 0; st < KSTEPS; ++st) {
-            if (st + 1 < KSTEPS) read_frags(s, as, bs, st + 1, y[(st + 1) & 1], x[(st + 1) & 1]);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = mfma_chunk<DT>(x[st & 1][fn], y[st & 1][fm], acc[fm][fn]);
-        }
-        if constexpr (!RR) {
-            constexpr int NR = FM + FN;                       // LDS reads per step
-            constexpr int NM = FM * FN * MFMA_PER_BLOCK;      // MFMAs per step
-            constexpr int PAIRS = NR < NM ? NR : NM;
-            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // step-0 reads
-#pragma unroll
-            for (int st = 0; st + 1 < KSTEPS; ++st) {
-#pragma unroll
-                for (int i = 0; i < PAIRS; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                if constexpr (NR > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NR - PAIRS, 0);
-                if constexpr (NM > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, NM - PAIRS, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    // Ask the scheduler to alternate MFMAs with `reads` LDS reads and
+    // `vmem` global loads, so that both hide under matrix-core time: after
+    // MFMA number I come its share of the reads and loads.
+    template <int reads, int vmem, int I = 0>
+    __device__ static __forceinline__ void interleave() {
+        if constexpr (I < NM) {
+            constexpr int per = (reads + NM - 1) / NM, vper = (vmem + NM - 1) / NM;
+            constexpr int rdone = I * per < reads ? I * per : reads;
+            constexpr int vdone = I * vper < vmem ? I * vper : vmem;
+            constexpr int rr = reads - rdone < per ? reads - rdone : per;
+            constexpr int vv = vmem - vdone < vper ? vmem - vdone : vper;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (rr > 0) __builtin_amdgcn_sched_group_barrier(0x100, rr, 0);
+            if constexpr (vv > 0) __builtin_amdgcn_sched_group_barrier(0x020, vv, 0);
+            interleave<reads, vmem, I + 1>();
         }
     }
 
-    // Tiles issued after kt that may still be in flight when kt is needed.
-    __device__ static __forceinline__ void wait_tile_direct(int ahead) {
-        if constexpr (STAGES >= 2) {
-            if (ahead >= STAGES - 2) { wait_vmcnt<LPT * (STAGES - 2)>(); return; }
+    // Global loads of the next tile are spread over the first KSTEPS-1
+    // steps of the current one: step st issues chunks [LD0(st), LD0(st+1)).
+    // A burst of loads would fill the address unit's queue and stall this
+    // wave's (in-order) MFMA issue behind it.
+    static constexpr int LD0(int st) {
+        return (LPT * st + KSTEPS - 2) / (KSTEPS - 1) < LPT ? (LPT * st + KSTEPS - 2) / (KSTEPS - 1) : LPT;
+    }
+
+    // Steps 0 .. KSTEPS-2 of the K-tile in `slot`.  On entry f[0] holds step
+    // 0's fragments; each step reads the next step's fragments while its
+    // MFMAs run (a two-deep register pipeline) and issues its share of the
+    // loads of K-tile `load_kt` (into LDS slot `load_slot` for DIRECT, into
+    // the register set `regs` for REG; none when DO_LOAD is false).
+    // KSTEPS is even, so on exit f[1] holds the last step's fragments and
+    // f[0] is free for the next tile's first step.
+    template <bool DO_LOAD, int ST = 0>
+    __device__ static __forceinline__ void tile_body(const State& s, uint8_t PG_LDS* smem, int slot,
+                                                     Frags (&f)[2], acc_t (&acc)[FM][FN], int load_kt,
+                                                     int load_slot, i32x4 (&regs)[LPT]) {
+        static_assert(KSTEPS % 2 == 0, "step parity");
+        if constexpr (ST + 1 < KSTEPS) {
+            constexpr int j0 = DO_LOAD ? LD0(ST) : 0, j1 = DO_LOAD ? LD0(ST + 1) : 0;
+            read_frags(s, smem, slot, ST + 1, f[(ST + 1) & 1]);
+            if constexpr (j1 > j0) {
+                if constexpr (VARIANT == VAR_DIRECT) issue_direct<j0, j1>(s, smem, load_kt, load_slot);
+                else gload<j0, j1>(s, regs, load_kt);
+            }
+            mfma_step(f[ST & 1], acc);
+            interleave<NR, j1 - j0>();
+            tile_body<DO_LOAD, ST + 1>(s, smem, slot, f, acc, load_kt, load_slot, regs);
         }
-        if constexpr (STAGES >= 4) { if (ahead == 1) { wait_vmcnt<LPT>(); return; } }
-        wait_vmcnt<0>();
     }
 
     __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
@@ -368,69 +400,97 @@ struct Gemm {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0;
 
+        // Every loop below is the K-tile loop restructured into prologue /
+        // main loop / drain.  Each K-tile runs steps 0..KSTEPS-2 (tile_body);
+        // the hand-over to the next tile -- wait for its data, barrier,
+        // refill the ring slot every wave has finished with, read the next
+        // tile's first fragments -- is issued before the last step's MFMAs,
+        // so the matrix cores stay busy across the tile boundary.
         const int nt = s.nt;
-        if constexpr (VARIANT == VAR_DIRECT) {
-            if constexpr (STAGES == 1) {
-                for (int kt = 0; kt < nt; ++kt) {
-                    issue_direct(s, smem, kt, 0);
-                    wait_vmcnt<0>();
-                    block_sync();
-                    compute(s, smem, 0, acc);
-                    block_sync();
-                }
-            } else {
-                // prologue: fill STAGES-1 slots
-#pragma unroll
-                for (int t = 0; t < STAGES - 1; ++t)
-                    if (t < nt) issue_direct(s, smem, t, t);
-                int slot = 0;
-                for (int kt = 0; kt < nt; ++kt) {
-                    wait_tile_direct(nt - 1 - kt);   // tile kt landed (this wave's part)
-                    block_sync();                    // ...every wave's part; slot kt-1 free
-                    if (kt + STAGES - 1 < nt)
-                        issue_direct(s, smem, kt + STAGES - 1, slot == 0 ? STAGES - 1 : slot - 1);
-                    compute(s, smem, slot, acc);
-                    slot = (slot + 1 == STAGES) ? 0 : slot + 1;
-                }
+        Frags f[2];
+        if constexpr (VARIANT == VAR_DIRECT && STAGES == 1) {
+            // Unpipelined: load, wait, barrier, compute, barrier.
+            i32x4 none[LPT];
+            for (int kt = 0; kt < nt; ++kt) {
+                issue_direct<0, LPT>(s, smem, kt, 0);
+                wait_vmcnt<0>();
+                block_sync();
+                read_frags(s, smem, 0, 0, f[0]);
+                tile_body<false>(s, smem, 0, f, acc, 0, 0, none);
+                mfma_step(f[1], acc);
+                interleave<0, 0>();
+                block_sync();
             }
+        } else if constexpr (VARIANT == VAR_DIRECT) {
+            // Ring of STAGES slots.  The prologue fills STAGES-1 of them; while
+            // tile kt is multiplied the loads of tile kt+STAGES-1 go into the
+            // slot tile kt-1 used.  Tiles at or past nt are still issued:
+            // every one of their offsets is out of the buffer's range, so they
+            // move no data and only write zeros into a slot no later tile
+            // reads.  The number of loads in flight is then the same at every
+            // boundary, so each wait is a fixed vmcnt and the body has no
+            // branch.  (The hand-over also runs after the last tile; the
+            // fragments it reads are never used.)
+            i32x4 none[LPT];
+#pragma unroll
+            for (int t = 0; t < STAGES - 1; ++t) issue_direct<0, LPT>(s, smem, t, t);
+            wait_vmcnt<(STAGES - 2) * LPT>();
+            block_sync();
+            read_frags(s, smem, 0, 0, f[0]);
+            int slot = 0;
+            for (int kt = 0; kt < nt; ++kt) {
+                const int prev = (slot == 0) ? STAGES - 1 : slot - 1;
+                const int next = (slot + 1 == STAGES) ? 0 : slot + 1;
+                tile_body<true>(s, smem, slot, f, acc, kt + STAGES - 1, prev, none);
+                wait_vmcnt<(STAGES - 2) * LPT>();     // tile kt+1 landed (this wave)
+                block_sync();                        // ...all waves; slot of kt free
+                read_frags(s, smem, next, 0, f[0]);
+                mfma_step(f[1], acc);
+                interleave<NR, 0>();
+                slot = next;
+            }
+            wait_vmcnt<0>();   // no LDS write may outlive the loop
         } else {
             i32x4 regs[RSETS][LPT];
             if constexpr (STAGES == 1) {
-                if (nt > 0) {
-                    gload(s, regs[0], 0);
-                    swrite(s, smem, regs[0], 0);
-                }
+                // One LDS buffer, one register set: tile kt+1 is loaded into
+                // registers while tile kt is multiplied (register prefetch).
+                gload<0, LPT>(s, regs[0], 0);
+                swrite(s, smem, regs[0], 0);
                 block_sync();
-                if (1 < nt) gload(s, regs[0], 1);
+                read_frags(s, smem, 0, 0, f[0]);
                 for (int kt = 0; kt < nt; ++kt) {
-                    compute(s, smem, 0, acc);
-                    if (kt + 1 < nt) {
-                        block_sync();                 // every wave done reading the slot
-                        swrite(s, smem, regs[0], 0);  // tile kt+1
-                        block_sync();
-                        if (kt + 2 < nt) gload(s, regs[0], kt + 2);
-                    }
+                    tile_body<true>(s, smem, 0, f, acc, kt + 1, 0, regs[0]);
+                    block_sync();                 // every wave done reading the buffer
+                    swrite(s, smem, regs[0], 0);  // tile kt+1 (zeros past the end)
+                    block_sync();
+                    read_frags(s, smem, 0, 0, f[0]);
+                    mfma_step(f[1], acc);
+                    interleave<NR, 0>();
                 }
             } else {
+                // Two LDS buffers, R = STAGES-1 register sets: tile j travels
+                // in set j % R; while tile kt is multiplied, tile kt+R is
+                // loaded into the set tile kt has just left.
                 constexpr int R = RSETS;
 #pragma unroll
-                for (int t = 0; t < R; ++t)
-                    if (t < nt) gload(s, regs[t], t);
-                if (nt > 0) swrite(s, smem, regs[0], 0);
-                if (R < nt) gload(s, regs[0], R);
+                for (int t = 0; t < R; ++t) gload<0, LPT>(s, regs[t], t);
+                swrite(s, smem, regs[0], 0);
                 block_sync();
+                read_frags(s, smem, 0, 0, f[0]);
                 for (int kb = 0; kb < nt; kb += R) {
 #pragma unroll
                     for (int i = 0; i < R; ++i) {
                         const int kt = kb + i;
                         if (kt < nt) {
-                            compute(s, smem, kt & 1, acc);
-                            if (kt + 1 < nt) {
-                                // tile kt+1 sits in set (kt+1) % R == (i+1) % R
-                                swrite(s, smem, regs[(i + 1) % R], (kt + 1) & 1);
-                                if (kt + 1 + R < nt) gload(s, regs[(i + 1) % R], kt + 1 + R);
-                                block_sync();
-                            }
+                            tile_body<true>(s, smem, kt & 1, f, acc, kt + R, 0, regs[i]);
+                            // buffer (kt+1)&1 was last read in iteration kt-1,
+                            // before that iteration's barrier
+                            swrite(s, smem, regs[(i + 1) % R], (kt + 1) & 1);
+                            block_sync();
+                            read_frags(s, smem, (kt + 1) & 1, 0, f[0]);
+                            mfma_step(f[1], acc);
+                            interleave<NR, 0>();
                         }
                     }
                 }

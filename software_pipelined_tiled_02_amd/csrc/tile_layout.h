@@ -16,12 +16,14 @@
 // order, lane-contiguous (one 16-byte chunk per lane per instruction), which
 // is the only order the direct-to-LDS load can produce.  Inside a row the
 // chunk a row's logical chunk c lives in is c ^ swz(row): an XOR swizzle that
-// costs no LDS bytes (padding would cost 1/cpr of the tile) and spreads the
-// 16-byte reads of 8 or 16 consecutive rows at one logical chunk over all
-// banks, whether the LDS serves 8 lanes x 16 B (32 banks) or 16 lanes x 16 B
-// (64 banks) per clock.  The padding/swizzling remedy for shared-memory bank
-// conflicts is the next step the pipelining study names (Detailed Analysis,
-// item 5).
+// costs no LDS bytes (padding would cost 1/cpr of the tile).  The MFMA
+// fragment read has lane l fetch row (l % 32) at chunk (c0 + l / 32); gfx950's
+// LDS has 64 banks of 4 bytes and serves a 16-byte read 16 lanes per clock,
+// so the swizzle makes every 16 consecutive rows at one logical chunk land in
+// 16 different 16-byte bank groups.  Each swizzle below was also measured
+// conflict-free for exactly this read on the hardware (SQ_LDS_BANK_CONFLICT).
+// The padding/swizzling remedy for shared-memory bank conflicts is the next
+// step the pipelining study names (Detailed Analysis, item 5).
 #ifndef PIPEGEMM_TILE_LAYOUT_H
 #define PIPEGEMM_TILE_LAYOUT_H
 
@@ -97,7 +99,7 @@ constexpr int loads_b(int dt, int tc, int stages) {
 constexpr int swz(int cpr, int row) {
     return cpr >= 16 ? (row & 15)
          : cpr == 8  ? ((row & 7) ^ ((row >> 3) & 3))
-         : cpr == 4  ? (((row >> 1) ^ (row >> 3)) & 3)
+         : cpr == 4  ? ((row >> 2) & 3)
                      : 0;
 }
 // Physical chunk index (within the tile) of logical (row, chunk).
