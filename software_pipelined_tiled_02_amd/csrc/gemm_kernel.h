@@ -262,67 +262,119 @@ struct Gemm {
         }
     }
 
-    __device__ static __forceinline__ void mfma_step(const Frags& f, acc_t (&acc)[FM][FN]) {
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = mfma_chunk<DT>(f.x[fn], f.y[fm], acc[fm][fn]);
-    }
+    // ---- the MFMA step schedule -------------------------------------------
+    //
+    // One step = the FM x FN MFMA blocks of one k-slice.  Each block is a
+    // "unit" of the schedule: its MFMA(s), then its share of the next step's
+    // fragment reads, then its share of global loads, closed by a scheduling
+    // fence so the compiler keeps exactly this order (it still inserts every
+    // wait the data dependences need).  Reads go early in the step, so the
+    // next step's first MFMAs never wait on LDS; loads are spread evenly, so
+    // the address unit's queue never fills and stalls the wave's in-order
+    // MFMA issue behind it.
+    static constexpr int NU = FM * FN;      // units per step
+    static constexpr int NRU = FM + FN;     // fragment reads per step (A-side first)
+    static constexpr int HALF = LPT / 2;    // loads issued right after the barrier
+    static constexpr int LSTEPS = KSTEPS - 1 < 2 ? KSTEPS - 1 : 2;   // body steps carrying the rest
+    static constexpr int rd_lo(int u) { return u * ((NRU + NU - 1) / NU) < NRU ? u * ((NRU + NU - 1) / NU) : NRU; }
 
-    static constexpr int MFMA_PER_BLOCK = (DT == DT_F32) ? 4 : 1;
-    static constexpr int NR = RR ? FM + FN * EPC : FM + FN;   // LDS read instructions per step
-    static constexpr int NM = FM * FN * MFMA_PER_BLOCK;        // MFMA instructions per step
-
-    // Ask the scheduler to alternate MFMAs with `reads` LDS reads and
-    // `vmem` global loads, so that both hide under matrix-core time: after
-    // MFMA number I come its share of the reads and loads.
-    template <int reads, int vmem, int I = 0>
-    __device__ static __forceinline__ void interleave() {
-        if constexpr (I < NM) {
-            constexpr int per = (reads + NM - 1) / NM, vper = (vmem + NM - 1) / NM;
-            constexpr int rdone = I * per < reads ? I * per : reads;
-            constexpr int vdone = I * vper < vmem ? I * vper : vmem;
-            constexpr int rr = reads - rdone < per ? reads - rdone : per;
-            constexpr int vv = vmem - vdone < vper ? vmem - vdone : vper;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (rr > 0) __builtin_amdgcn_sched_group_barrier(0x100, rr, 0);
-            if constexpr (vv > 0) __builtin_amdgcn_sched_group_barrier(0x020, vv, 0);
-            interleave<reads, vmem, I + 1>();
+    // Fragment read r of step st of the K-tile in `slot`.
+    __device__ static __forceinline__ void read_one(const State& s, const uint8_t PG_LDS* smem, int slot,
+                                                    int st, int r, Frags& f) {
+        const uint8_t PG_LDS* as = slot_ptr(smem, slot);
+        const uint8_t PG_LDS* bs = as + A_BYTES;
+        const int lane = s.tid & 63;
+        if (r < FM) {
+            f.y[r] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + r * 32) * CPR * kChunk + s.rd[st]);
+        } else {
+            const int fn = r - FM;
+            if constexpr (RR)
+                f.x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
+            else
+                f.x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
         }
     }
 
-    // Global loads of the next tile are spread over the first KSTEPS-1
-    // steps of the current one: step st issues chunks [LD0(st), LD0(st+1)).
-    // A burst of loads would fill the address unit's queue and stall this
-    // wave's (in-order) MFMA issue behind it.
-    static constexpr int LD0(int st) {
-        return (LPT * st + KSTEPS - 2) / (KSTEPS - 1) < LPT ? (LPT * st + KSTEPS - 2) / (KSTEPS - 1) : LPT;
+    // Load chunk j of K-tile kt: into LDS slot `slot` (DIRECT) or regs[j] (REG).
+    __device__ static __forceinline__ void load_one(const State& s, uint8_t PG_LDS* smem, int kt, int slot,
+                                                    i32x4 (&regs)[LPT], int j) {
+        if constexpr (VARIANT == VAR_DIRECT) {
+            uint8_t PG_LDS* base = smem + slot * SLOT;
+            if (j < LA)
+                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
+            else
+                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, off_b(s, j - LA, kt));
+        } else {
+            if (j < LA)
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
+            else
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j - LA, kt), 0, 0);
+        }
+    }
+
+    // One step: MFMAs on `cur`; if RD, read step rd_st of rd_slot into `nxt`;
+    // load chunks [J0, J1) of tile ld_kt.  (Called with constant arguments and
+    // fully unrolled: every index below is a constant, so fragments and
+    // accumulators stay in registers.)
+    template <bool RD>
+    __device__ static __forceinline__ void step(const State& s, uint8_t PG_LDS* smem, const Frags& cur,
+                                                Frags& nxt, int rd_slot, int rd_st, acc_t (&acc)[FM][FN],
+                                                int J0, int J1, int ld_kt, int ld_slot, i32x4 (&regs)[LPT]) {
+        const int NL = J1 - J0;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int fm = u / FN, fn = u % FN;
+            acc[fm][fn] = mfma_chunk<DT>(cur.x[fn], cur.y[fm], acc[fm][fn]);
+            if constexpr (RD) {
+#pragma unroll
+                for (int r = rd_lo(u); r < rd_lo(u + 1); ++r) read_one(s, smem, rd_slot, rd_st, r, nxt);
+            }
+#pragma unroll
+            for (int j = J0 + u * NL / NU; j < J0 + (u + 1) * NL / NU; ++j)
+                load_one(s, smem, ld_kt, ld_slot, regs, j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // Steps 0 .. KSTEPS-2 of the K-tile in `slot`.  On entry f[0] holds step
-    // 0's fragments; each step reads the next step's fragments while its
-    // MFMAs run (a two-deep register pipeline) and issues its share of the
-    // loads of K-tile `load_kt` (into LDS slot `load_slot` for DIRECT, into
-    // the register set `regs` for REG; none when DO_LOAD is false).
-    // KSTEPS is even, so on exit f[1] holds the last step's fragments and
-    // f[0] is free for the next tile's first step.
-    template <bool DO_LOAD, int ST = 0>
+    // 0's fragments; each step reads the next step's while its MFMAs run (a
+    // two-deep register pipeline).  When LOADS, the first LSTEPS steps also
+    // carry chunks [HALF, LPT) of K-tile ld_kt (the chunks [0, HALF) went out
+    // right after the previous barrier).  KSTEPS is even, so on exit f[1]
+    // holds the last step's fragments and f[0] is free for the next tile.
+    template <bool LOADS>
     __device__ static __forceinline__ void tile_body(const State& s, uint8_t PG_LDS* smem, int slot,
-                                                     Frags (&f)[2], acc_t (&acc)[FM][FN], int load_kt,
-                                                     int load_slot, i32x4 (&regs)[LPT]) {
+                                                     Frags (&f)[2], acc_t (&acc)[FM][FN], int ld_kt,
+                                                     int ld_slot, i32x4 (&regs)[LPT]) {
         static_assert(KSTEPS % 2 == 0, "step parity");
-        if constexpr (ST + 1 < KSTEPS) {
-            constexpr int j0 = DO_LOAD ? LD0(ST) : 0, j1 = DO_LOAD ? LD0(ST + 1) : 0;
-            read_frags(s, smem, slot, ST + 1, f[(ST + 1) & 1]);
-            if constexpr (j1 > j0) {
-                if constexpr (VARIANT == VAR_DIRECT) issue_direct<j0, j1>(s, smem, load_kt, load_slot);
-                else gload<j0, j1>(s, regs, load_kt);
-            }
-            mfma_step(f[ST & 1], acc);
-            interleave<NR, j1 - j0>();
-            tile_body<DO_LOAD, ST + 1>(s, smem, slot, f, acc, load_kt, load_slot, regs);
+        constexpr int REST = LPT - HALF;
+#pragma unroll
+        for (int st = 0; st + 1 < KSTEPS; ++st) {
+            const int j0 = (LOADS && st < LSTEPS) ? HALF + st * REST / LSTEPS : 0;
+            const int j1 = (LOADS && st < LSTEPS) ? HALF + (st + 1) * REST / LSTEPS : 0;
+            step<true>(s, smem, f[st & 1], f[(st + 1) & 1], slot, st + 1, acc, j0, j1, ld_kt, ld_slot, regs);
         }
+    }
+
+    // Read every fragment of step 0 of `slot` into f (no MFMA to overlap).
+    __device__ static __forceinline__ void read_first(const State& s, const uint8_t PG_LDS* smem, int slot, Frags& f) {
+#pragma unroll
+        for (int r = 0; r < NRU; ++r) read_one(s, smem, slot, 0, r, f);
+    }
+
+    // One K-tile of the register-staged ring with R staging sets: tile kt
+    // travels in set i = kt % R; while it is multiplied, tile kt+R is loaded
+    // into set i, which tile kt has just left.
+    template <int R>
+    __device__ static __forceinline__ void reg_tile(const State& s, uint8_t PG_LDS* smem, Frags (&f)[2],
+                                                    acc_t (&acc)[FM][FN], i32x4 (&regs)[RSETS][LPT], int kt,
+                                                    int i) {
+        tile_body<true>(s, smem, kt & 1, f, acc, kt + R, 0, regs[i]);
+        // buffer (kt+1)&1 was last read in iteration kt-1, before that
+        // iteration's barrier
+        swrite(s, smem, regs[(i + 1) % R], (kt + 1) & 1);
+        block_sync();
+        step<true>(s, smem, f[1], f[0], (kt + 1) & 1, 0, acc, 0, HALF, kt + 1 + R, 0, regs[(i + 1) % R]);
     }
 
     __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
@@ -406,6 +458,17 @@ struct Gemm {
         // refill the ring slot every wave has finished with, read the next
         // tile's first fragments -- is issued before the last step's MFMAs,
         // so the matrix cores stay busy across the tile boundary.
+        // Every loop below is the K-tile loop restructured into prologue /
+        // main loop / drain.  Each K-tile runs steps 0..KSTEPS-2 (tile_body);
+        // the hand-over to the next tile -- wait for its data, barrier, read
+        // its first fragments, start refilling the slot every wave has just
+        // finished with -- runs under the last step's MFMAs.  Tiles at or past
+        // nt are still loaded: every one of their offsets is out of the
+        // buffer's range, so they move no data and only write zeros into a
+        // slot (or register set) no later tile reads.  The number of loads in
+        // flight is then the same at every boundary, so each wait is a fixed
+        // vmcnt and the loop body has no branch.  (The hand-over also runs
+        // after the last tile; the fragments it reads are never used.)
         const int nt = s.nt;
         Frags f[2];
         if constexpr (VARIANT == VAR_DIRECT && STAGES == 1) {
@@ -415,28 +478,22 @@ struct Gemm {
                 issue_direct<0, LPT>(s, smem, kt, 0);
                 wait_vmcnt<0>();
                 block_sync();
-                read_frags(s, smem, 0, 0, f[0]);
+                read_first(s, smem, 0, f[0]);
                 tile_body<false>(s, smem, 0, f, acc, 0, 0, none);
-                mfma_step(f[1], acc);
-                interleave<0, 0>();
+                step<false>(s, smem, f[1], f[0], 0, 0, acc, 0, 0, 0, 0, none);
                 block_sync();
             }
         } else if constexpr (VARIANT == VAR_DIRECT) {
-            // Ring of STAGES slots.  The prologue fills STAGES-1 of them; while
-            // tile kt is multiplied the loads of tile kt+STAGES-1 go into the
-            // slot tile kt-1 used.  Tiles at or past nt are still issued:
-            // every one of their offsets is out of the buffer's range, so they
-            // move no data and only write zeros into a slot no later tile
-            // reads.  The number of loads in flight is then the same at every
-            // boundary, so each wait is a fixed vmcnt and the body has no
-            // branch.  (The hand-over also runs after the last tile; the
-            // fragments it reads are never used.)
+            // Ring of STAGES slots: while tile kt is multiplied, tiles
+            // kt+1 .. kt+STAGES-1 are in flight; tile kt+STAGES-1 goes into
+            // the slot tile kt-1 used.
             i32x4 none[LPT];
 #pragma unroll
             for (int t = 0; t < STAGES - 1; ++t) issue_direct<0, LPT>(s, smem, t, t);
             wait_vmcnt<(STAGES - 2) * LPT>();
             block_sync();
-            read_frags(s, smem, 0, 0, f[0]);
+            read_first(s, smem, 0, f[0]);
+            issue_direct<0, HALF>(s, smem, STAGES - 1, STAGES - 1);
             int slot = 0;
             for (int kt = 0; kt < nt; ++kt) {
                 const int prev = (slot == 0) ? STAGES - 1 : slot - 1;
@@ -444,9 +501,7 @@ struct Gemm {
                 tile_body<true>(s, smem, slot, f, acc, kt + STAGES - 1, prev, none);
                 wait_vmcnt<(STAGES - 2) * LPT>();     // tile kt+1 landed (this wave)
                 block_sync();                        // ...all waves; slot of kt free
-                read_frags(s, smem, next, 0, f[0]);
-                mfma_step(f[1], acc);
-                interleave<NR, 0>();
+                step<true>(s, smem, f[1], f[0], next, 0, acc, 0, HALF, kt + STAGES, slot, none);
                 slot = next;
             }
             wait_vmcnt<0>();   // no LDS write may outlive the loop
@@ -458,15 +513,14 @@ struct Gemm {
                 gload<0, LPT>(s, regs[0], 0);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
-                read_frags(s, smem, 0, 0, f[0]);
+                read_first(s, smem, 0, f[0]);
+                gload<0, HALF>(s, regs[0], 1);
                 for (int kt = 0; kt < nt; ++kt) {
                     tile_body<true>(s, smem, 0, f, acc, kt + 1, 0, regs[0]);
                     block_sync();                 // every wave done reading the buffer
                     swrite(s, smem, regs[0], 0);  // tile kt+1 (zeros past the end)
                     block_sync();
-                    read_frags(s, smem, 0, 0, f[0]);
-                    mfma_step(f[1], acc);
-                    interleave<NR, 0>();
+                    step<true>(s, smem, f[1], f[0], 0, 0, acc, 0, HALF, kt + 2, 0, regs[0]);
                 }
             } else {
                 // Two LDS buffers, R = STAGES-1 register sets: tile j travels
@@ -477,22 +531,17 @@ struct Gemm {
                 for (int t = 0; t < R; ++t) gload<0, LPT>(s, regs[t], t);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
-                read_frags(s, smem, 0, 0, f[0]);
+                read_first(s, smem, 0, f[0]);
+                gload<0, HALF>(s, regs[0], R);
+                // Whole groups of R tiles, so that set indices are constants
+                // (a guard inside the unrolled group makes the compiler
+                // spill).  The up to R-1 tiles past nt hold zeros only: the
+                // accumulators start at +0, and adding exact zero products
+                // under round-to-nearest leaves every accumulator bit as it
+                // was, so C is unchanged.
                 for (int kb = 0; kb < nt; kb += R) {
 #pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        const int kt = kb + i;
-                        if (kt < nt) {
-                            tile_body<true>(s, smem, kt & 1, f, acc, kt + R, 0, regs[i]);
-                            // buffer (kt+1)&1 was last read in iteration kt-1,
-                            // before that iteration's barrier
-                            swrite(s, smem, regs[(i + 1) % R], (kt + 1) & 1);
-                            block_sync();
-                            read_frags(s, smem, (kt + 1) & 1, 0, f[0]);
-                            mfma_step(f[1], acc);
-                            interleave<NR, 0>();
-                        }
-                    }
+                    for (int i = 0; i < R; ++i) reg_tile<R>(s, smem, f, acc, regs, kb + i, i);
                 }
             }
         }
