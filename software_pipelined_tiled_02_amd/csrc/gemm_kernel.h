@@ -108,13 +108,6 @@ __device__ __forceinline__ void block_sync() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 template <int DT, int LAYOUT, int TC, int STAGES, int VARIANT>
 struct Gemm {
     static constexpr TileShape TS = tile_shape(TC);
@@ -546,54 +539,83 @@ struct Gemm {
             }
         }
 
-        // Epilogue: lane holds C[m][n .. n+3] of each 32x32 block.
+        // Epilogue: lane holds C[m][n .. n+3] of each 32x32 block.  A wave
+        // whose whole block lies inside C (every wave but those on the
+        // bottom/right edge) stores without any per-element test.
         const int t = lane & 31, h = lane >> 5;
+        const int mw = m0 + s.wm * WTM, nw = n0 + s.wn * WTN;
+        if (mw + WTM <= args.M && nw + WTN <= args.N) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int m = m0 + s.wm * WTM + fm * 32 + t;
-            if (m >= args.M) continue;
-            uint8_t* crow = (uint8_t*)args.C + (int64_t)m * args.ldc * OSZ;
+            for (int fm = 0; fm < FM; ++fm) {
+                uint8_t* crow = (uint8_t*)args.C + (int64_t)(mw + fm * 32 + t) * args.ldc * OSZ;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
+                for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = n0 + s.wn * WTN + fn * 32 + 8 * q + 4 * h;
-                    store4(crow, n, args.N, acc[fm][fn], q);
+                    for (int q = 0; q < 4; ++q)
+                        store4_full(crow, nw + fn * 32 + 8 * q + 4 * h, acc[fm][fn], q);
+            }
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int m = mw + fm * 32 + t;
+                if (m >= args.M) continue;
+                uint8_t* crow = (uint8_t*)args.C + (int64_t)m * args.ldc * OSZ;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = nw + fn * 32 + 8 * q + 4 * h;
+                        store4(crow, n, args.N, acc[fm][fn], q);
+                    }
                 }
             }
         }
     }
 
-    __device__ static __forceinline__ void store4(uint8_t* crow, int n, int N, const acc_t& a, int q) {
-        if constexpr (DT == DT_I8 || DT == DT_F32) {
-            const i32x16 ai = __builtin_bit_cast(i32x16, a);   // whole-vector cast
-            i32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = ai[4 * q + e];
-            if (n + 4 <= N) {
-                *(i32x4*)(crow + (int64_t)n * 4) = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) *(int*)(crow + (int64_t)(n + e) * 4) = v[e];
-            }
+    // Four consecutive outputs of one row as stored: int32/fp32 as they are,
+    // fp16/bf16 rounded to nearest even by the hardware conversion.
+    __device__ static __forceinline__ i32x4 out4_32(const acc_t& a, int q) {
+        const i32x16 ai = __builtin_bit_cast(i32x16, a);   // whole-vector cast
+        return i32x4{ai[4 * q], ai[4 * q + 1], ai[4 * q + 2], ai[4 * q + 3]};
+    }
+    __device__ static __forceinline__ i32x2 out4_16(const acc_t& a, int q) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 lo = {a[4 * q], a[4 * q + 1]}, hi = {a[4 * q + 2], a[4 * q + 3]};
+        if constexpr (DT == DT_BF16) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            return i32x2{__builtin_bit_cast(int, __builtin_convertvector(lo, bf16x2)),
+                         __builtin_bit_cast(int, __builtin_convertvector(hi, bf16x2))};
         } else {
-            uint16_t hv[4];
+            typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+            return i32x2{__builtin_bit_cast(int, __builtin_convertvector(lo, f16x2)),
+                         __builtin_bit_cast(int, __builtin_convertvector(hi, f16x2))};
+        }
+    }
+
+    __device__ static __forceinline__ void store4_full(uint8_t* crow, int n, const acc_t& a, int q) {
+        if constexpr (DT == DT_I8 || DT == DT_F32)
+            *(i32x4*)(crow + (int64_t)n * 4) = out4_32(a, q);
+        else
+            *(i32x2*)(crow + (int64_t)n * 2) = out4_16(a, q);
+    }
+
+    // Masked version for blocks on the bottom/right edge of C.
+    __device__ static __forceinline__ void store4(uint8_t* crow, int n, int N, const acc_t& a, int q) {
+        if (n + 4 <= N) {
+            store4_full(crow, n, a, q);
+            return;
+        }
+        if constexpr (DT == DT_I8 || DT == DT_F32) {
+            const i32x4 v = out4_32(a, q);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (DT == DT_BF16) hv[e] = f32_to_bf16_rne(a[4 * q + e]);
-                else hv[e] = __builtin_bit_cast(uint16_t, (_Float16)a[4 * q + e]);
-            }
-            if (n + 4 <= N) {
-                i32x2 v;
-                v[0] = (int)(hv[0] | ((uint32_t)hv[1] << 16));
-                v[1] = (int)(hv[2] | ((uint32_t)hv[3] << 16));
-                *(i32x2*)(crow + (int64_t)n * 2) = v;
-            } else {
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) *(int*)(crow + (int64_t)(n + e) * 4) = v[e];
+        } else {
+            const i32x2 v = out4_16(a, q);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) *(uint16_t*)(crow + (int64_t)(n + e) * 2) = hv[e];
-            }
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N)
+                    *(uint16_t*)(crow + (int64_t)(n + e) * 2) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
         }
     }
 };
