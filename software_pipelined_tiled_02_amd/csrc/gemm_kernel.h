@@ -32,9 +32,16 @@
 // Any k order inside an MFMA is fine as long as both operands use the same
 // one, which they do by construction.
 //
-// Edges.  Rows past M (or N) and K-columns past K are loaded as zeros: the
-// lane's buffer offset is replaced by one beyond the buffer's range, and an
-// out-of-range buffer load returns 0 (also into LDS).  Stores are masked.
+// Addressing.  Each lane's buffer offset of a chunk is fixed for the whole
+// K loop; the K-tile's position goes into the instruction's scalar offset,
+// so the loop spends no vector instructions on addresses.  Rows past M (or
+// columns past N) read a valid row of the tile instead: they only feed
+// outputs that are never stored.  A ragged last K-tile is multiplied first
+// (logical tile 0, loaded in the prologue), so it is the only load that
+// needs a per-lane test: its chunks past K get an offset beyond the
+// buffer's range, and an out-of-range buffer load returns 0 (also into
+// LDS).  Tiles past the last one get an out-of-range scalar offset and load
+// zeros.  Stores are masked.
 #ifndef PIPEGEMM_GEMM_KERNEL_H
 #define PIPEGEMM_GEMM_KERNEL_H
 
@@ -145,52 +152,70 @@ struct Gemm {
         uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
         uint32_t kb_step;              // byte advance of the B offset per K-tile
-        int K, nt;
+        int K, nt, tail;               // tail: K is not a multiple of BK
         int tid, wave, wm, wn;
     };
 
-    __device__ static __forceinline__ void lds_dma(const State& s, bool is_a, uint8_t PG_LDS* dst, uint32_t off) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? s.ra : s.rb, (void PG_LDS*)dst, 16, off, 0, 0, 0);
+    __device__ static __forceinline__ void lds_dma(const State& s, bool is_a, uint8_t PG_LDS* dst, uint32_t voff,
+                                                   uint32_t soff) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? s.ra : s.rb, (void PG_LDS*)dst, 16, voff, soff, 0, 0);
     }
 
-    // Byte offset of this lane's j-th chunk of K-tile kt, or kOob.
-    __device__ static __forceinline__ uint32_t off_a(const State& s, int j, int kt) {
-        uint32_t off = s.offa[j] + (uint32_t)kt * (uint32_t)(BK * SZ);
-        if ((kt + 1) * BK > s.K && s.kca[j] + (uint32_t)kt * BK >= (uint32_t)s.K) off = kOob;
-        return off;
+    // K-tile order: with a ragged last tile, that tile is logical tile 0 and
+    // the full tiles follow in order; otherwise the order is unchanged.
+    __device__ static __forceinline__ int phys_tile(const State& s, int t) {
+        return s.tail ? (t == 0 ? s.nt - 1 : t - 1) : t;
     }
-    __device__ static __forceinline__ uint32_t off_b(const State& s, int j, int kt) {
-        uint32_t off = s.offb[j] + (uint32_t)kt * s.kb_step;
-        if ((kt + 1) * BK > s.K && s.kcb[j] + (uint32_t)kt * BK >= (uint32_t)s.K) off = kOob;
-        return off;
+    // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
+    // tile, an offset that takes every lane out of the buffer's range.
+    __device__ static __forceinline__ uint32_t soff_a(const State& s, int t) {
+        return t < s.nt ? (uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ) : kOob;
+    }
+    __device__ static __forceinline__ uint32_t soff_b(const State& s, int t) {
+        return t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob;
+    }
+    // Per-lane offset of chunk j.  FIRST: the chunk belongs to logical tile
+    // 0, which may be the ragged one; chunks starting at or past K move out
+    // of range.
+    template <bool FIRST>
+    __device__ static __forceinline__ uint32_t voff_a(const State& s, int j) {
+        if (FIRST && s.kca[j] + (uint32_t)(s.nt - 1) * BK >= (uint32_t)s.K) return kOob;
+        return s.offa[j];
+    }
+    template <bool FIRST>
+    __device__ static __forceinline__ uint32_t voff_b(const State& s, int j) {
+        if (FIRST && s.kcb[j] + (uint32_t)(s.nt - 1) * BK >= (uint32_t)s.K) return kOob;
+        return s.offb[j];
     }
 
     // DIRECT: issue chunks J0 .. J1-1 of K-tile kt into LDS slot `slot`
     // (chunks 0 .. LA-1 are the A tile, LA .. LPT-1 the B tile).  Chunk j of
     // wave w lands at physical chunk j*T + 64*w + lane, the order LDS-DMA
     // writes in; the lane's source chunk is the logical one stored there.
-    template <int J0, int J1>
+    template <int J0, int J1, bool FIRST = false>
     __device__ static __forceinline__ void issue_direct(const State& s, uint8_t PG_LDS* smem, int kt, int slot) {
         uint8_t PG_LDS* base = smem + slot * SLOT;
+        const uint32_t sa = soff_a(s, kt), sb = soff_b(s, kt);
 #pragma unroll
         for (int j = J0; j < J1; ++j) {
             if (j < LA)
-                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
+                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, voff_a<FIRST>(s, j), sa);
             else
-                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, off_b(s, j - LA, kt));
+                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, voff_b<FIRST>(s, j - LA), sb);
         }
     }
 
     // REG: load chunks J0 .. J1-1 of K-tile kt into a VGPR staging set /
     // store a whole set into a slot.
-    template <int J0, int J1>
+    template <int J0, int J1, bool FIRST = false>
     __device__ static __forceinline__ void gload(const State& s, i32x4 (&r)[LPT], int kt) {
+        const uint32_t sa = soff_a(s, kt), sb = soff_b(s, kt);
 #pragma unroll
         for (int j = J0; j < J1; ++j) {
             if (j < LA)
-                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
+                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, voff_a<FIRST>(s, j), sa, 0);
             else
-                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j - LA, kt), 0, 0);
+                r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, voff_b<FIRST>(s, j - LA), sb, 0);
         }
     }
     __device__ static __forceinline__ void swrite(const State& s, uint8_t PG_LDS* smem, const i32x4 (&r)[LPT], int slot) {
@@ -288,20 +313,22 @@ struct Gemm {
         }
     }
 
-    // Load chunk j of K-tile kt: into LDS slot `slot` (DIRECT) or regs[j] (REG).
+    // Load chunk j of logical K-tile kt (never tile 0): into LDS slot `slot`
+    // (DIRECT) or regs[j] (REG).
     __device__ static __forceinline__ void load_one(const State& s, uint8_t PG_LDS* smem, int kt, int slot,
                                                     i32x4 (&regs)[LPT], int j) {
         if constexpr (VARIANT == VAR_DIRECT) {
             uint8_t PG_LDS* base = smem + slot * SLOT;
             if (j < LA)
-                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, off_a(s, j, kt));
+                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, s.offa[j], soff_a(s, kt));
             else
-                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, off_b(s, j - LA, kt));
+                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, s.offb[j - LA],
+                        soff_b(s, kt));
         } else {
             if (j < LA)
-                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, off_a(s, j, kt), 0, 0);
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.offa[j], soff_a(s, kt), 0);
             else
-                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, off_b(s, j - LA, kt), 0, 0);
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.offb[j - LA], soff_b(s, kt), 0);
         }
     }
 
@@ -397,6 +424,7 @@ struct Gemm {
 
         s.K = args.K;
         s.nt = (args.K + BK - 1) / BK;
+        s.tail = (args.K % BK) != 0;
         const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
         const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
                               : (const uint8_t*)args.B + (int64_t)n0 * args.ldb * SZ;
@@ -408,7 +436,8 @@ struct Gemm {
         for (int j = 0; j < LA; ++j) {
             const int p = j * T + s.tid;
             const int r = logical_row(CPR, p), c = logical_chunk(CPR, p);
-            s.offa[j] = (m0 + r < args.M) ? (uint32_t)r * lda_b + (uint32_t)(c * EPC * SZ) : kOob;
+            const int rr = (m0 + r < args.M) ? r : 0;
+            s.offa[j] = (uint32_t)rr * lda_b + (uint32_t)(c * EPC * SZ);
             s.kca[j] = (uint32_t)(c * EPC);
         }
         if constexpr (RR) {
@@ -417,7 +446,8 @@ struct Gemm {
             for (int j = 0; j < LB; ++j) {
                 const int p = j * T + s.tid;
                 const int r = p / CPR_BRR, c = p % CPR_BRR;
-                s.offb[j] = (n0 + c * EPC < args.N) ? (uint32_t)r * ldb_b + (uint32_t)(c * EPC * SZ) : kOob;
+                const int cc = (n0 + c * EPC < args.N) ? c : 0;
+                s.offb[j] = (uint32_t)r * ldb_b + (uint32_t)(cc * EPC * SZ);
                 s.kcb[j] = (uint32_t)r;
             }
             s.kb_step = (uint32_t)BK * ldb_b;
@@ -426,7 +456,8 @@ struct Gemm {
             for (int j = 0; j < LB; ++j) {
                 const int p = j * T + s.tid;
                 const int r = logical_row(CPR, p), c = logical_chunk(CPR, p);
-                s.offb[j] = (n0 + r < args.N) ? (uint32_t)r * ldb_b + (uint32_t)(c * EPC * SZ) : kOob;
+                const int rr = (n0 + r < args.N) ? r : 0;
+                s.offb[j] = (uint32_t)rr * ldb_b + (uint32_t)(c * EPC * SZ);
                 s.kcb[j] = (uint32_t)(c * EPC);
             }
             s.kb_step = (uint32_t)(BK * SZ);
@@ -447,12 +478,6 @@ struct Gemm {
 
         // Every loop below is the K-tile loop restructured into prologue /
         // main loop / drain.  Each K-tile runs steps 0..KSTEPS-2 (tile_body);
-        // the hand-over to the next tile -- wait for its data, barrier,
-        // refill the ring slot every wave has finished with, read the next
-        // tile's first fragments -- is issued before the last step's MFMAs,
-        // so the matrix cores stay busy across the tile boundary.
-        // Every loop below is the K-tile loop restructured into prologue /
-        // main loop / drain.  Each K-tile runs steps 0..KSTEPS-2 (tile_body);
         // the hand-over to the next tile -- wait for its data, barrier, read
         // its first fragments, start refilling the slot every wave has just
         // finished with -- runs under the last step's MFMAs.  Tiles at or past
@@ -465,24 +490,28 @@ struct Gemm {
         const int nt = s.nt;
         Frags f[2];
         if constexpr (VARIANT == VAR_DIRECT && STAGES == 1) {
-            // Unpipelined: load, wait, barrier, compute, barrier.
+            // Unpipelined: load, wait, barrier, compute, barrier.  (The
+            // load of tile kt+1 is issued at the end of iteration kt.)
             i32x4 none[LPT];
+            issue_direct<0, LPT, true>(s, smem, 0, 0);
             for (int kt = 0; kt < nt; ++kt) {
-                issue_direct<0, LPT>(s, smem, kt, 0);
                 wait_vmcnt<0>();
                 block_sync();
                 read_first(s, smem, 0, f[0]);
                 tile_body<false>(s, smem, 0, f, acc, 0, 0, none);
                 step<false>(s, smem, f[1], f[0], 0, 0, acc, 0, 0, 0, 0, none);
                 block_sync();
+                issue_direct<0, LPT>(s, smem, kt + 1, 0);
             }
+            wait_vmcnt<0>();   // no LDS write may outlive the loop
         } else if constexpr (VARIANT == VAR_DIRECT) {
             // Ring of STAGES slots: while tile kt is multiplied, tiles
             // kt+1 .. kt+STAGES-1 are in flight; tile kt+STAGES-1 goes into
             // the slot tile kt-1 used.
             i32x4 none[LPT];
+            issue_direct<0, LPT, true>(s, smem, 0, 0);
 #pragma unroll
-            for (int t = 0; t < STAGES - 1; ++t) issue_direct<0, LPT>(s, smem, t, t);
+            for (int t = 1; t < STAGES - 1; ++t) issue_direct<0, LPT>(s, smem, t, t);
             wait_vmcnt<(STAGES - 2) * LPT>();
             block_sync();
             read_first(s, smem, 0, f[0]);
@@ -503,7 +532,7 @@ struct Gemm {
             if constexpr (STAGES == 1) {
                 // One LDS buffer, one register set: tile kt+1 is loaded into
                 // registers while tile kt is multiplied (register prefetch).
-                gload<0, LPT>(s, regs[0], 0);
+                gload<0, LPT, true>(s, regs[0], 0);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
                 read_first(s, smem, 0, f[0]);
@@ -520,8 +549,9 @@ struct Gemm {
                 // in set j % R; while tile kt is multiplied, tile kt+R is
                 // loaded into the set tile kt has just left.
                 constexpr int R = RSETS;
+                gload<0, LPT, true>(s, regs[0], 0);
 #pragma unroll
-                for (int t = 0; t < R; ++t) gload<0, LPT>(s, regs[t], t);
+                for (int t = 1; t < R; ++t) gload<0, LPT>(s, regs[t], t);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
                 read_first(s, smem, 0, f[0]);

@@ -30,13 +30,16 @@ class Violation(AssertionError):
 def direct_program(S, nt, fault=None):
     ev = []
     if S == 1:
+        ev.append(("load", 0, 0, 0, LPT))
         for kt in range(nt):
-            ev.append(("load", kt, 0, 0, LPT))
             ev.append(("wait", 0 if fault != "wait" else LPT))
             ev.append(("barrier",))
             ev.append(("read", 0, kt))
             if fault != "barrier":
                 ev.append(("barrier",))
+            ev.append(("load", kt + 1, 0, 0, LPT))
+        if fault != "drain":
+            ev.append(("wait", 0))
         return ev
     for t in range(S - 1):
         ev.append(("load", t, t, 0, LPT))
