@@ -133,7 +133,7 @@ struct Gemm {
     static constexpr int SLOT = A_BYTES + B_BYTES;
     static constexpr int SLOTS = lds_slots(VARIANT, STAGES);
     static constexpr int RSETS = reg_sets(VARIANT, STAGES);
-    static constexpr int LDS = SLOT * SLOTS;
+    static constexpr int LDS = lds_bytes(DT, TC, STAGES, VARIANT);   // the ring, or the epilogue strips
     static constexpr bool RR = (LAYOUT == LAYOUT_RR);
     static constexpr int CPR_BRR = BN * SZ / kChunk;       // chunks per row of a K x N B tile
     typedef typename AccT<DT>::type acc_t;
@@ -569,36 +569,71 @@ struct Gemm {
             }
         }
 
-        // Epilogue: lane holds C[m][n .. n+3] of each 32x32 block.  A wave
-        // whose whole block lies inside C (every wave but those on the
-        // bottom/right edge) stores without any per-element test.
+        // Epilogue.  Lane (t, h) holds C[m][n .. n+3] of each 32x32 block
+        // (m = row t of the block, n = 8q + 4h), so a direct store would
+        // scatter 8-16 bytes over 32 rows per instruction.  Instead each
+        // wave stages one 32-row strip of its block at a time in a private
+        // LDS region and reads it back row-contiguously: every store
+        // instruction then writes whole rows of the wave's block, 16 bytes
+        // per lane.  The ring is free once every wave has drained its loads
+        // and crossed the barrier below.
+        block_sync();
         const int t = lane & 31, h = lane >> 5;
         const int mw = m0 + s.wm * WTM, nw = n0 + s.wn * WTN;
-        if (mw + WTM <= args.M && nw + WTN <= args.N) {
+        uint8_t PG_LDS* strip = smem + s.wave * STRIP_BYTES;
+        const bool full = (mw + WTM <= args.M) && (nw + WTN <= args.N);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                uint8_t* crow = (uint8_t*)args.C + (int64_t)(mw + fm * 32 + t) * args.ldc * OSZ;
+        for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        store4_full(crow, nw + fn * 32 + 8 * q + 4 * h, acc[fm][fn], q);
-            }
-        } else {
+                for (int q = 0; q < 4; ++q) {
+                    uint8_t PG_LDS* dst = strip + t * STRIP_ROW + (fn * 32 + 8 * q + 4 * h) * OSZ;
+                    if constexpr (OSZ == 4)
+                        *(i32x4 PG_LDS*)dst = out4_32(acc[fm][fn], q);
+                    else
+                        *(i32x2 PG_LDS*)dst = out4_16(acc[fm][fn], q);
+                }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int m = mw + fm * 32 + t;
-                if (m >= args.M) continue;
-                uint8_t* crow = (uint8_t*)args.C + (int64_t)m * args.ldc * OSZ;
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int n = nw + fn * 32 + 8 * q + 4 * h;
-                        store4(crow, n, args.N, acc[fm][fn], q);
-                    }
+            for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
+                const int r = i * ROWS_PER_STORE + lane / LANES_PER_ROW;
+                const int c = (lane % LANES_PER_ROW) * (kChunk / OSZ);   // column in the wave block
+                const i32x4 v = *(const i32x4 PG_LDS*)(strip + r * STRIP_ROW + c * OSZ);
+                const int m = mw + fm * 32 + r, n = nw + c;
+                uint8_t* dst = (uint8_t*)args.C + ((int64_t)m * args.ldc + n) * OSZ;
+                if (full) {
+                    *(i32x4*)dst = v;
+                } else if (m < args.M) {
+                    store_part(dst, n, args.N, v);
                 }
             }
+        }
+    }
+
+    // Staging strip of the epilogue: 32 rows of one wave's block, each row
+    // padded by 16 bytes so that the 32 rows written at one column fall in
+    // different LDS banks.
+    static constexpr int STRIP_ROW = strip_row_bytes(DT, TC);
+    static constexpr int STRIP_BYTES = 32 * STRIP_ROW;
+    static constexpr int LANES_PER_ROW = WTN * OSZ / kChunk;
+    static constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
+    static_assert(64 % LANES_PER_ROW == 0 && 32 % ROWS_PER_STORE == 0, "epilogue store shape");
+    static_assert(STRIP_BYTES * WM * WN <= LDS && SLOT * SLOTS <= LDS, "LDS layout");
+
+    // Store the chunk v (16 bytes, columns n ..) of a row on the right edge:
+    // whole if it lies inside C, else element by element.
+    __device__ static __forceinline__ void store_part(uint8_t* dst, int n, int N, const i32x4 v) {
+        constexpr int E = kChunk / OSZ;
+        if (n + E <= N) {
+            *(i32x4*)dst = v;
+        } else if constexpr (OSZ == 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) *(int*)(dst + e * 4) = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N) *(uint16_t*)(dst + e * 2) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
         }
     }
 
@@ -622,32 +657,6 @@ struct Gemm {
         }
     }
 
-    __device__ static __forceinline__ void store4_full(uint8_t* crow, int n, const acc_t& a, int q) {
-        if constexpr (DT == DT_I8 || DT == DT_F32)
-            *(i32x4*)(crow + (int64_t)n * 4) = out4_32(a, q);
-        else
-            *(i32x2*)(crow + (int64_t)n * 2) = out4_16(a, q);
-    }
-
-    // Masked version for blocks on the bottom/right edge of C.
-    __device__ static __forceinline__ void store4(uint8_t* crow, int n, int N, const acc_t& a, int q) {
-        if (n + 4 <= N) {
-            store4_full(crow, n, a, q);
-            return;
-        }
-        if constexpr (DT == DT_I8 || DT == DT_F32) {
-            const i32x4 v = out4_32(a, q);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < N) *(int*)(crow + (int64_t)(n + e) * 4) = v[e];
-        } else {
-            const i32x2 v = out4_16(a, q);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < N)
-                    *(uint16_t*)(crow + (int64_t)(n + e) * 2) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
-        }
-    }
 };
 
 template <int DT, int LAYOUT, int TC, int STAGES, int VARIANT>

@@ -80,8 +80,20 @@ constexpr int tiles_in_flight(int variant, int stages) {
 constexpr int slot_bytes(int dt, int tc, int stages) {
     return (tile_shape(tc).bm + tile_shape(tc).bn) * block_k(dt, tc, stages) * in_size(dt);
 }
-constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
+constexpr int ring_bytes(int dt, int tc, int stages, int variant) {
     return slot_bytes(dt, tc, stages) * lds_slots(variant, stages);
+}
+// The epilogue reuses LDS to stage one 32-row strip of C per wave; a strip
+// row is the wave's block width plus 16 bytes of padding (bank spreading).
+constexpr int strip_row_bytes(int dt, int tc) {
+    return tile_shape(tc).bn / tile_shape(tc).wn * out_size(dt) + kChunk;
+}
+constexpr int epilogue_bytes(int dt, int tc) {
+    return 32 * strip_row_bytes(dt, tc) * tile_shape(tc).wm * tile_shape(tc).wn;
+}
+constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
+    return ring_bytes(dt, tc, stages, variant) > epilogue_bytes(dt, tc) ? ring_bytes(dt, tc, stages, variant)
+                                                                        : epilogue_bytes(dt, tc);
 }
 constexpr int threads(int tc) { return tile_shape(tc).wm * tile_shape(tc).wn * 64; }
 
