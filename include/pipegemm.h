@@ -97,10 +97,12 @@ typedef struct {
     int32_t tiles_in_flight; /* K-tiles loading while one is multiplied */
     int32_t lds_bytes;       /* LDS per workgroup */
     int32_t loads_per_tile;  /* 16-byte loads per lane per K-tile */
-    int64_t grid;            /* workgroups */
+    int64_t grid;            /* workgroups launched */
     int64_t k_tiles;         /* ceil(K / block_k) */
     int32_t k_tail;          /* K mod block_k; 0 means no ragged last tile */
-    int32_t reserved;
+    int32_t c_tiles;         /* C tiles; above grid when each workgroup of the
+                                256x256 tile computes several in turn (then
+                                grid = one workgroup per CU) */
 } gemm_config_info_t;
 
 /* Bind a handle to HIP device `device`.  Allocates host memory for the

@@ -106,7 +106,12 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.tiles_in_flight = pg::tiles_in_flight(variant, stages);
     in.lds_bytes = pg::lds_bytes(dtype, tc, stages, variant);
     in.loads_per_tile = pg::loads_a(dtype, tc, stages) + pg::loads_b(dtype, tc, stages);
-    in.grid = tm * tn;
+    // The 256x256 tile runs one workgroup per CU (its LDS ring and
+    // registers allow no second one); with more tiles than CUs, a grid of
+    // one workgroup per CU loops over the tiles, so that one tile's C stores
+    // overlap the next tile's first loads.
+    in.c_tiles = (int32_t)(tm * tn);
+    in.grid = (tc == pg::TILE_L && tm * tn > num_cus && num_cus % 8 == 0) ? num_cus : tm * tn;
     in.k_tiles = ceil_div(K, bk);
     in.k_tail = (int32_t)(K % bk);
     plan->tile = tc;

@@ -397,7 +397,19 @@ struct Gemm {
         step<true>(s, smem, f[1], f[0], (kt + 1) & 1, 0, acc, 0, HALF, kt + 1 + R, 0, regs[(i + 1) % R]);
     }
 
+    // Each workgroup computes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+    // (one tile when the grid covers C; several when the host launches one
+    // workgroup per CU, so that a tile's C stores overlap the next tile's
+    // prologue loads).
     __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
+        const int ntiles = args.tiles_m * args.tiles_n;
+        for (int j = blockIdx.x; j < ntiles; j += gridDim.x) {
+            if (j != (int)blockIdx.x) block_sync();   // every wave is done with the last strips
+            run_tile(args, smem, j, ntiles);
+        }
+    }
+
+    __device__ static __forceinline__ void run_tile(const GemmArgs args, uint8_t PG_LDS* smem, int j, int ntiles) {
         State s;
         s.tid = threadIdx.x;
         s.wave = __builtin_amdgcn_readfirstlane(s.tid >> 6);
@@ -405,13 +417,13 @@ struct Gemm {
         s.wn = s.wave % WN;
         const int lane = s.tid & 63;
 
-        // Workgroup -> C tile.  Workgroups are handed to the 8 XCDs round
-        // robin; regroup so that each XCD gets a contiguous run of tiles, and
-        // order the runs in bands of kGroupM tile-rows so that the tiles one
-        // XCD holds at a time share A rows and B columns in its L2.
-        int w = blockIdx.x;
-        const int G = gridDim.x;
-        if ((G & 7) == 0) w = (w & 7) * (G >> 3) + (w >> 3);
+        // Tile index -> C tile.  Workgroups are handed to the 8 XCDs round
+        // robin, so tile j runs on XCD j % 8 (the grid is a multiple of 8);
+        // regroup so that each XCD gets a contiguous run of tiles, and order
+        // the runs in bands of kGroupM tile-rows so that the tiles one XCD
+        // holds at a time share A rows and B columns in its L2.
+        int w = j;
+        if ((ntiles & 7) == 0 && (gridDim.x & 7) == 0) w = (w & 7) * (ntiles >> 3) + (w >> 3);
         constexpr int kGroupM = 4;
         const int band = kGroupM * args.tiles_n;
         const int g = w / band;
@@ -602,7 +614,8 @@ struct Gemm {
                 const int m = mw + fm * 32 + r, n = nw + c;
                 uint8_t* dst = (uint8_t*)args.C + ((int64_t)m * args.ldc + n) * OSZ;
                 if (full) {
-                    *(i32x4*)dst = v;
+                    // C is written once and not read here: stream it past the caches.
+                    __builtin_nontemporal_store(v, (i32x4*)dst);
                 } else if (m < args.M) {
                     store_part(dst, n, args.N, v);
                 }

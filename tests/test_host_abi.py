@@ -100,7 +100,9 @@ def test_auto_tile_choice():
     assert q(M=2048, N=2048)[1]["tile"] == binding.GEMM_TILE_128x128  # 64 big tiles < 256 CUs
     assert q(dtype="f32", layout="RR", M=256, N=256, K=256)[1]["tile"] == binding.GEMM_TILE_32x64
     info = q(M=8192, N=8192, K=8200, stages=4)[1]
-    assert (info["grid"], info["k_tiles"], info["k_tail"], info["block_k"]) == (1024, 257, 8, 32)
+    assert (info["c_tiles"], info["k_tiles"], info["k_tail"], info["block_k"]) == (1024, 257, 8, 32)
+    assert info["grid"] == 256          # one workgroup per CU, four tiles each
+    assert q()[1]["grid"] == q()[1]["c_tiles"] == 256
 
 
 def test_status_strings():
