@@ -600,17 +600,25 @@ struct Gemm {
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    uint8_t PG_LDS* dst = strip + t * STRIP_ROW + (fn * 32 + 8 * q + 4 * h) * OSZ;
-                    if constexpr (OSZ == 4)
-                        *(i32x4 PG_LDS*)dst = out4_32(acc[fm][fn], q);
-                    else
-                        *(i32x2 PG_LDS*)dst = out4_16(acc[fm][fn], q);
+                    if constexpr (OSZ == 4) {
+                        *(i32x4 PG_LDS*)(strip + t * STRIP_ROW + (fn * 32 + 8 * q + 4 * h) * 4) = out4_32(acc[fm][fn], q);
+                    } else {
+                        // Rows 8..15 and 24..31 keep the two 8-byte halves
+                        // of each 16-byte chunk swapped: with rows 32 bytes
+                        // apart (mod 256), rows t and t+8 then fill the
+                        // complementary halves of the same banks.
+                        const int hs = h ^ ((t >> 3) & 1);
+                        *(i32x2 PG_LDS*)(strip + t * STRIP_ROW + (fn * 32 + 8 * q) * 2 + 8 * hs) = out4_16(acc[fm][fn], q);
+                    }
                 }
 #pragma unroll
             for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
                 const int r = i * ROWS_PER_STORE + lane / LANES_PER_ROW;
                 const int c = (lane % LANES_PER_ROW) * (kChunk / OSZ);   // column in the wave block
-                const i32x4 v = *(const i32x4 PG_LDS*)(strip + r * STRIP_ROW + c * OSZ);
+                i32x4 v = *(const i32x4 PG_LDS*)(strip + r * STRIP_ROW + c * OSZ);
+                if constexpr (OSZ == 2) {
+                    if ((r >> 3) & 1) v = i32x4{v[2], v[3], v[0], v[1]};
+                }
                 const int m = mw + fm * 32 + r, n = nw + c;
                 uint8_t* dst = (uint8_t*)args.C + ((int64_t)m * args.ldc + n) * OSZ;
                 if (full) {
@@ -624,8 +632,8 @@ struct Gemm {
     }
 
     // Staging strip of the epilogue: 32 rows of one wave's block, each row
-    // padded by 16 bytes so that the 32 rows written at one column fall in
-    // different LDS banks.
+    // padded so that the rows written at one column fall in different LDS
+    // banks (see strip_row_bytes).
     static constexpr int STRIP_ROW = strip_row_bytes(DT, TC);
     static constexpr int STRIP_BYTES = 32 * STRIP_ROW;
     static constexpr int LANES_PER_ROW = WTN * OSZ / kChunk;

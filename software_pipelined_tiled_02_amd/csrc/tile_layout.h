@@ -84,9 +84,12 @@ constexpr int ring_bytes(int dt, int tc, int stages, int variant) {
     return slot_bytes(dt, tc, stages) * lds_slots(variant, stages);
 }
 // The epilogue reuses LDS to stage one 32-row strip of C per wave; a strip
-// row is the wave's block width plus 16 bytes of padding (bank spreading).
+// row is the wave's block width plus padding that spreads the rows over the
+// LDS banks: 16 bytes for 4-byte outputs (16-byte stores, one row per lane),
+// 32 bytes for 2-byte outputs (each lane stores two 8-byte pieces 16 bytes
+// apart, so consecutive rows must start 32 bytes apart).
 constexpr int strip_row_bytes(int dt, int tc) {
-    return tile_shape(tc).bn / tile_shape(tc).wn * out_size(dt) + kChunk;
+    return tile_shape(tc).bn / tile_shape(tc).wn * out_size(dt) + (out_size(dt) == 2 ? 2 * kChunk : kChunk);
 }
 constexpr int epilogue_bytes(int dt, int tc) {
     return 32 * strip_row_bytes(dt, tc) * tile_shape(tc).wm * tile_shape(tc).wn;

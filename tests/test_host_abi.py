@@ -87,8 +87,9 @@ def test_large_tile_budget(dtype, bk2, bk4):
             assert info["lds_slots"] == slots
             ring = slots * (256 + 256) * bk * sz
             # the epilogue stages 32 rows of each wave's 128-column block of C
-            # (4-byte outputs for int8/fp32, 2-byte for fp16/bf16), rows padded by 16 B
-            strips = 4 * 32 * (128 * (4 if dtype in ("i8", "f32") else 2) + 16)
+            # (4-byte outputs for int8/fp32, rows padded by 16 B; 2-byte for
+            # fp16/bf16, rows padded by 32 B)
+            strips = 4 * 32 * (128 * 4 + 16 if dtype in ("i8", "f32") else 128 * 2 + 32)
             assert info["lds_bytes"] == max(ring, strips) <= 160 * 1024
             assert info["reg_sets"] == (0 if variant == "direct" else max(1, stages - 1))
             assert info["tiles_in_flight"] == (stages - 1 if variant == "direct" else max(1, stages - 1))
