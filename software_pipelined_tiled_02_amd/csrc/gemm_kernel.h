@@ -37,7 +37,7 @@
 // so the loop spends no vector instructions on addresses.  Rows past M (or
 // columns past N) read a valid row of the tile instead: they only feed
 // outputs that are never stored.  A ragged last K-tile is multiplied first
-// (logical tile 0, loaded in the prologue), so it is the only load that
+// (loaded in the prologue; see phys_tile), so it is the only load that
 // needs a per-lane test: its chunks past K get an offset beyond the
 // buffer's range, and an out-of-range buffer load returns 0 (also into
 // LDS).  Tiles past the last one get an out-of-range scalar offset and load
@@ -152,8 +152,9 @@ struct Gemm {
         uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
         uint32_t kb_step;              // byte advance of the B offset per K-tile
-        int K, nt, tail;               // tail: K is not a multiple of BK
-        int nfull, rot;                // full K-tiles; the one the loop starts at
+        int K, nt;
+        int head;                      // K-tiles of the ragged head (0, 1 or 2)
+        int nbody, rot;                // the other K-tiles; the one they start at
         int tid, wave, wm, wn;
     };
 
@@ -162,13 +163,17 @@ struct Gemm {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? s.ra : s.rb, (void PG_LDS*)dst, 16, voff, soff, 0, 0);
     }
 
-    // K-tile order: with a ragged last tile, that tile is logical tile 0;
-    // the full tiles follow in order, starting at full tile `rot` and
-    // wrapping around.
+    // K-tile order.  When K is not a multiple of BKMAX (the K-tile of the
+    // class's 1-2 stage instances), the K columns past the last multiple of
+    // BKMAX -- `head` tiles, the last one ragged -- are multiplied first, in
+    // order; the other tiles follow in order, starting at `rot` and wrapping
+    // around.  The head is defined by BKMAX rather than BK so that instances
+    // with BK = BKMAX / 2 add the same k-slices in the same order, and every
+    // (stages, variant) pair gives bit-identical C.
     __device__ static __forceinline__ int phys_tile(const State& s, int t) {
-        if (s.tail && t == 0) return s.nt - 1;
-        const int q = (s.tail ? t - 1 : t) + s.rot;
-        return q >= s.nfull ? q - s.nfull : q;
+        if (t < s.head) return s.nbody + t;
+        const int q = t - s.head + s.rot;
+        return q >= s.nbody ? q - s.nbody : q;
     }
     // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
     // tile, an offset that takes every lane out of the buffer's range.
@@ -178,9 +183,9 @@ struct Gemm {
     __device__ static __forceinline__ uint32_t soff_b(const State& s, int t) {
         return t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob;
     }
-    // Per-lane offset of chunk j.  FIRST: the chunk belongs to logical tile
-    // 0, which may be the ragged one; chunks starting at or past K move out
-    // of range.
+    // Per-lane offset of chunk j.  FIRST: the chunk belongs to the last
+    // physical K-tile (logical tile head-1), which may be ragged; chunks
+    // starting at or past K move out of range.
     template <bool FIRST>
     __device__ static __forceinline__ uint32_t voff_a(const State& s, int j) {
         if (FIRST && s.kca[j] + (uint32_t)(s.nt - 1) * BK >= (uint32_t)s.K) return kOob;
@@ -228,6 +233,21 @@ struct Gemm {
         for (int j = 0; j < LA; ++j) base[j * T + s.tid] = r[j];
 #pragma unroll
         for (int j = 0; j < LB; ++j) base[A_BYTES / kChunk + j * T + s.tid] = r[LA + j];
+    }
+
+    // Prologue load of all of logical K-tile t, with the per-lane K test
+    // when t is the last physical tile (the ragged one, if any).
+    __device__ static __forceinline__ void first_direct(const State& s, uint8_t PG_LDS* smem, int t, int slot) {
+        if (t == s.head - 1)
+            issue_direct<0, LPT, true>(s, smem, t, slot);
+        else
+            issue_direct<0, LPT>(s, smem, t, slot);
+    }
+    __device__ static __forceinline__ void first_gload(const State& s, i32x4 (&r)[LPT], int t) {
+        if (t == s.head - 1)
+            gload<0, LPT, true>(s, r, t);
+        else
+            gload<0, LPT>(s, r, t);
     }
 
     // RR B fragment: gather the EPC k-consecutive elements of one column.
@@ -440,8 +460,13 @@ struct Gemm {
 
         s.K = args.K;
         s.nt = (args.K + BK - 1) / BK;
-        s.tail = (args.K % BK) != 0;
-        s.nfull = s.nt - s.tail;
+        {
+            constexpr int BKMAX = block_k(DT, TC, 1);
+            static_assert(BKMAX % BK == 0 && (BKMAX == BK || STAGES >= 3), "head tiles are all in the prologue");
+            const int rem = args.K % BKMAX;
+            s.head = (rem + BK - 1) / BK;
+            s.nbody = s.nt - s.head;
+        }
         // Start the K loop of the tiles on XCD x at full tile 9x (mod the
         // count): with every XCD reading the same K columns at once, the
         // row-strided reads of A pile onto the same HBM channels (measured on
@@ -449,7 +474,7 @@ struct Gemm {
         // tiles keep a common K position, so they still share B in its L2.
         // The 256x256 tile keeps the plain order: its bands share A and B
         // across each XCD's tiles and gain nothing from it.
-        s.rot = (TC != TILE_L && s.nfull > 0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)s.nfull) : 0;
+        s.rot = (TC != TILE_L && s.nbody > 0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)s.nbody) : 0;
         const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
         const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
                               : (const uint8_t*)args.B + (int64_t)n0 * args.ldb * SZ;
@@ -518,7 +543,7 @@ struct Gemm {
             // Unpipelined: load, wait, barrier, compute, barrier.  (The
             // load of tile kt+1 is issued at the end of iteration kt.)
             i32x4 none[LPT];
-            issue_direct<0, LPT, true>(s, smem, 0, 0);
+            first_direct(s, smem, 0, 0);
             for (int kt = 0; kt < nt; ++kt) {
                 wait_vmcnt<0>();
                 block_sync();
@@ -534,9 +559,8 @@ struct Gemm {
             // kt+1 .. kt+STAGES-1 are in flight; tile kt+STAGES-1 goes into
             // the slot tile kt-1 used.
             i32x4 none[LPT];
-            issue_direct<0, LPT, true>(s, smem, 0, 0);
 #pragma unroll
-            for (int t = 1; t < STAGES - 1; ++t) issue_direct<0, LPT>(s, smem, t, t);
+            for (int t = 0; t < STAGES - 1; ++t) first_direct(s, smem, t, t);
             wait_vmcnt<(STAGES - 2) * LPT>();
             block_sync();
             read_first(s, smem, 0, f[0]);
@@ -557,7 +581,7 @@ struct Gemm {
             if constexpr (STAGES == 1) {
                 // One LDS buffer, one register set: tile kt+1 is loaded into
                 // registers while tile kt is multiplied (register prefetch).
-                gload<0, LPT, true>(s, regs[0], 0);
+                first_gload(s, regs[0], 0);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
                 read_first(s, smem, 0, f[0]);
@@ -574,9 +598,8 @@ struct Gemm {
                 // in set j % R; while tile kt is multiplied, tile kt+R is
                 // loaded into the set tile kt has just left.
                 constexpr int R = RSETS;
-                gload<0, LPT, true>(s, regs[0], 0);
 #pragma unroll
-                for (int t = 1; t < R; ++t) gload<0, LPT>(s, regs[t], t);
+                for (int t = 0; t < R; ++t) first_gload(s, regs[t], t);
                 swrite(s, smem, regs[0], 0);
                 block_sync();
                 read_first(s, smem, 0, f[0]);

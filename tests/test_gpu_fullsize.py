@@ -78,3 +78,47 @@ def test_workload(g, name):
                 "%s S=%d %s differs bitwise from the first pair" % (name, stages, variant)
         del c
     torch.cuda.empty_cache()
+
+
+# More 256x256 tiles than CUs, so each workgroup loops over several tiles,
+# with ragged M, N and K edges: (M, N, K, dtype, dist, scale)
+PERSISTENT = {
+    "bf16_4100x4200x1000": (4100, 4200, 1000, "bf16", "uniform", 1.0),
+    "i8_4300x4120x1008": (4300, 4120, 1008, "i8", "int", 1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(PERSISTENT))
+def test_tile_loop_with_edges(name):
+    M, N, K, dtype, dist, scale = PERSISTENT[name]
+    print("workload:", name, flush=True)
+    gg = binding.Gemm(0)
+    try:
+        gg.set_tile("256x256")
+        _, info = binding.gemm_query(M, N, K, dtype, "RC", 2, "direct", tile="256x256")
+        assert info["c_tiles"] > info["grid"] == 256, info
+        a, b = inputs.make_operands(M, N, K, dtype, "RC", dist, seed=3, scale=scale)
+        rows, cols = sample_points(M, N, 3000, seed=4)
+        ref = oracle.gemm_entries(inputs.to_oracle(a, dtype), inputs.to_oracle(b, dtype), dtype, "RC",
+                                  rows, cols)
+        ad, bd = a.cuda(), b.cuda()
+        first = None
+        for stages, variant in [(2, "direct"), (1, "direct"), (3, "reg"), (4, "direct")]:
+            print("  stages=%d variant=%s" % (stages, variant), flush=True)
+            c = alloc_c(M, N, N, dtype)
+            binding.gemm_run(gg.h, M, N, K, dtype, "RC", stages, variant, ad, K, bd, K, c, N)
+            torch.cuda.synchronize()
+            got = inputs.from_torch_out(c[rows, cols], dtype)
+            if dtype == "i8":
+                assert np.array_equal(got, ref), (name, stages, variant)
+            else:
+                rms = float(np.sqrt(np.mean(ref ** 2)))
+                assert np.all(np.abs(got - ref) <= 1e-2 * np.abs(ref) + 1e-2 * rms), (name, stages, variant)
+            check_sentinel(c[M:], 0, N, dtype)
+            if first is None:
+                first = c
+            else:
+                assert torch.equal(c.view(torch.uint8), first.view(torch.uint8)), (name, stages, variant)
+    finally:
+        gg.close()
+    torch.cuda.empty_cache()
