@@ -163,17 +163,12 @@ struct Gemm {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? s.ra : s.rb, (void PG_LDS*)dst, 16, voff, soff, 0, 0);
     }
 
-    // K-tile order.  When K is not a multiple of BKMAX (the K-tile of the
-    // class's 1-2 stage instances), the K columns past the last multiple of
-    // BKMAX -- `head` tiles, the last one ragged -- are multiplied first, in
-    // order; the other tiles follow in order, starting at `rot` and wrapping
-    // around.  The head is defined by BKMAX rather than BK so that instances
+    // K-tile order (k_phys_tile): the ragged head first, then the rest from
+    // `rot`.  The head is defined by BKMAX rather than BK so that instances
     // with BK = BKMAX / 2 add the same k-slices in the same order, and every
     // (stages, variant) pair gives bit-identical C.
     __device__ static __forceinline__ int phys_tile(const State& s, int t) {
-        if (t < s.head) return s.nbody + t;
-        const int q = t - s.head + s.rot;
-        return q >= s.nbody ? q - s.nbody : q;
+        return k_phys_tile(t, s.head, s.nbody, s.rot);
     }
     // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
     // tile, an offset that takes every lane out of the buffer's range.
@@ -463,8 +458,7 @@ struct Gemm {
         {
             constexpr int BKMAX = block_k(DT, TC, 1);
             static_assert(BKMAX % BK == 0 && (BKMAX == BK || STAGES >= 3), "head tiles are all in the prologue");
-            const int rem = args.K % BKMAX;
-            s.head = (rem + BK - 1) / BK;
+            s.head = k_head_tiles(args.K, BK, BKMAX);
             s.nbody = s.nt - s.head;
         }
         // Start the K loop of the tiles on XCD x at full tile 9x (mod the

@@ -123,6 +123,17 @@ constexpr int phys_chunk(int cpr, int row, int chunk) { return row * cpr + (chun
 constexpr int logical_row(int cpr, int p) { return p / cpr; }
 constexpr int logical_chunk(int cpr, int p) { return (p % cpr) ^ swz(cpr, p / cpr); }
 
+// K-tile order of the K loop.  When K is not a multiple of bkmax (the
+// K-tile of the class's 1-2 stage instances), the `head` tiles covering the
+// K columns past the last multiple of bkmax -- the last of them ragged --
+// come first, in order; the other `nbody` tiles follow in order, starting
+// at tile `rot` and wrapping around.  Logical tile t is physical tile
+// k_phys_tile(t, ...).
+constexpr int k_head_tiles(int K, int bk, int bkmax) { return (K % bkmax + bk - 1) / bk; }
+constexpr int k_phys_tile(int t, int head, int nbody, int rot) {
+    return t < head ? nbody + t : (t - head + rot >= nbody ? t - head + rot - nbody : t - head + rot);
+}
+
 // Budget check of one instance: LDS ring within the CU's LDS, and every
 // per-lane load count a whole number.
 constexpr bool instance_fits(int dt, int tc, int stages, int variant) {

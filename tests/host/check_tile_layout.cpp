@@ -6,7 +6,9 @@
 //     in gfx950's LDS as measured: 64 banks of 4 bytes, a 16-byte read
 //     served 16 consecutive lanes per clock, so within each 16-lane group
 //     the 16-byte bank groups (address / 16 mod 16) hit must all differ;
-//  3. without the swizzle the same read does conflict (so 2 is not vacuous).
+//  3. without the swizzle the same read does conflict (so 2 is not vacuous);
+//  4. the K-tile order is a permutation with the ragged tile in the
+//     prologue, and every stage count adds the k-slices in one order.
 // Prints one line per chunks-per-row value; exits non-zero on failure.
 #include <cstdio>
 #include "tile_layout.h"
@@ -59,6 +61,45 @@ int main() {
             for (int s = 1; s <= kMaxStages; ++s)
                 for (int v = 0; v < 2; ++v)
                     if (!instance_fits(dt, tc, s, v)) { std::printf("over budget %d %d %d %d\n", dt, tc, s, v); ++fail; }
+    // K-tile order: a permutation of the tiles whose last physical tile (the
+    // ragged one) is logical tile head-1, and -- for the classes whose K-tile
+    // halves at 3-4 stages -- the same sequence of MFMA k-slices (2 chunks
+    // each) at both K-tile sizes, so all stage counts sum in one order.
+    int order_fail = 0;
+    for (int dt = 0; dt < 4; ++dt)
+        for (int tc = 0; tc < TILE_COUNT; ++tc) {
+            const int bkmax = block_k(dt, tc, 1), slice = 2 * epc(dt);
+            for (int K = 1; K <= 9 * bkmax; K += (K < 3 * bkmax ? 1 : 7)) {
+                int seq[2][1024], len[2] = {0, 0};
+                for (int s = 1; s <= kMaxStages; ++s) {
+                    const int bk = block_k(dt, tc, s), nt = (K + bk - 1) / bk;
+                    const int head = k_head_tiles(K, bk, bkmax), nbody = nt - head;
+                    if (head > (s == 1 ? 1 : s - 1)) ++order_fail;   // head tiles are prologue loads
+                    for (int rot = 0; rot < (nbody > 0 ? nbody : 1); rot += 1 + nbody / 5) {
+                        bool seen[2048] = {false};
+                        for (int t = 0; t < nt; ++t) {
+                            const int p = k_phys_tile(t, head, nbody, rot);
+                            if (p < 0 || p >= nt || seen[p]) ++order_fail;
+                            else seen[p] = true;
+                        }
+                        if (head > 0 && k_phys_tile(head - 1, head, nbody, rot) != nt - 1) ++order_fail;
+                    }
+                    if (s != 1 && s != 3) continue;
+                    int* q = seq[s == 1 ? 0 : 1];
+                    int& n = len[s == 1 ? 0 : 1];
+                    for (int t = 0; t < nt; ++t) {
+                        const int p = k_phys_tile(t, head, nbody, 0);
+                        for (int k0 = p * bk; k0 < (p + 1) * bk; k0 += slice)
+                            if (k0 < K && n < 1024) q[n++] = k0;
+                    }
+                }
+                if (len[0] != len[1]) ++order_fail;
+                for (int i = 0; i < len[0] && i < len[1]; ++i)
+                    if (seq[0][i] != seq[1][i]) { ++order_fail; break; }
+            }
+        }
+    std::printf("K-tile order: %s\n", order_fail ? "FAIL" : "permutation, ragged tile loaded first, one k-slice order for all stage counts");
+    fail += order_fail;
     std::printf(fail ? "FAIL (%d)\n" : "OK\n", fail);
     return fail ? 1 : 0;
 }
