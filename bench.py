@@ -7,9 +7,12 @@ A step is one C = A * B launch (the whole K-loop pipeline: prologue, main
 loop, drain, epilogue) over one synthetic input set.  After half a second
 of untimed launches that lets the GPU clocks settle, every (stages,
 variant) pair of the chosen workload is timed: W untimed warm-up steps,
-then exactly K steps, each bracketed by HIP events recorded on the stream
-the kernel is launched on.  Inputs rotate over enough copies that the
-footprint exceeds 512 MiB, so the 256 MB Infinity Cache cannot hold them.
+then exactly K steps launched back to back between two HIP events recorded
+on the stream the kernel is launched on (synchronised on both sides); the
+mean launch duration is that interval over K.  A second pass of K launches,
+each between its own events, gives the spread (per_launch_* in "sweep").
+Inputs rotate over enough copies that the footprint exceeds 512 MiB, so
+the 256 MB Infinity Cache cannot hold them.
 The headline is the fastest pair; all pairs are in "sweep".
 
 Prints one JSON line.  `value` is TOP/s (int8) or TFLOP/s (fp) counting
@@ -171,25 +174,32 @@ def main():
         for i in range(args.warmup):
             launch(i, s, v)
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+        # The timed region: K launches back to back between two events on
+        # the launch stream, synchronised on both sides.
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start.record(stream)
         for i in range(args.steps):
+            launch(i, s, v)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total = t_start.elapsed_time(t_end)                       # ms
+        mean = total / args.steps
+        # Spread (informational): the same K launches, each between its own
+        # pair of events (which adds the event records' gaps to each).
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for i in range(args.steps):
             ev[i][0].record(stream)
             launch(i, s, v)
             ev[i][1].record(stream)
-        t_end.record(stream)
         torch.cuda.synchronize()
         per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)       # ms per launch
-        mean = sum(per) / len(per)
-        total = t_start.elapsed_time(t_end)
         results[(s, v)] = {
             "mean_us": round(mean * 1e3, 2), "median_us": round(per[len(per) // 2] * 1e3, 2),
             "min_us": round(per[0] * 1e3, 2), "max_us": round(per[-1] * 1e3, 2),
-            "ms_per_step": total / args.steps,
+            "ms_per_step": mean,
             "tops": ops / (mean * 1e-3) / 1e12, "gbs": algo_bytes / (mean * 1e-3) / 1e9,
         }
         print("# %-14s S=%d %-6s mean %8.2f us  %8.1f %s  %7.1f GB/s" % (
@@ -224,8 +234,8 @@ def main():
                    "tile": "%dx%dx%d" % (info["block_m"], info["block_n"], info["block_k"]),
                    "lds_bytes": info["lds_bytes"], "grid": info["grid"]},
         "roofline": roof,
-        "sweep": {"S%d_%s" % p: {"us": q["mean_us"], "median_us": q["median_us"],
-                                 "min_us": q["min_us"], "max_us": q["max_us"],
+        "sweep": {"S%d_%s" % p: {"us": q["mean_us"], "per_launch_median_us": q["median_us"],
+                                 "per_launch_min_us": q["min_us"], "per_launch_max_us": q["max_us"],
                                  unit if bound != "hbm" else "GB/s":
                                      round(q["tops"] if bound != "hbm" else q["gbs"], 2),
                                  "frac_peak": round(q["tops"] / PEAK[dtype], 4) if bound != "hbm"
