@@ -33,8 +33,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool instance_exists(int layout, int tile) {
-    // layout RR is built at the 128x128 and 32x64 tiles only
-    return layout == pg::LAYOUT_RC || tile != pg::TILE_L;
+    // both layouts are built at every tile class
+    return (layout == pg::LAYOUT_RC || layout == pg::LAYOUT_RR) && tile >= 0 && tile < pg::TILE_COUNT;
 }
 
 // Every check of the ABI, then the configuration.  No HIP call.

@@ -136,6 +136,7 @@ struct Gemm {
     static constexpr int LDS = lds_bytes(DT, TC, STAGES, VARIANT);   // the ring, or the epilogue strips
     static constexpr bool RR = (LAYOUT == LAYOUT_RR);
     static constexpr int CPR_BRR = BN * SZ / kChunk;       // chunks per row of a K x N B tile
+    static constexpr int RB_RR = BN * SZ;                   // bytes per row of a K x N B tile
     typedef typename AccT<DT>::type acc_t;
 
     static_assert(instance_fits(DT, TC, STAGES, VARIANT), "instance over budget");
@@ -151,6 +152,7 @@ struct Gemm {
         uint32_t offa[LA], offb[LB];   // byte offsets at K-tile 0 (kOob if the row is outside)
         uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
+        uint32_t rrb[RR ? FN : 1];     // layout RR: per-lane B fragment read offset (step 0)
         uint32_t kb_step;              // byte advance of the B offset per K-tile
         int K, nt;
         int head;                      // K-tiles of the ragged head (0, 1 or 2)
@@ -172,11 +174,14 @@ struct Gemm {
     }
     // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
     // tile, an offset that takes every lane out of the buffer's range.
+    // (readfirstlane states what is true -- every lane holds the same value
+    // -- so that the compiler keeps the offset in a scalar register instead
+    // of looping over lanes.)
     __device__ static __forceinline__ uint32_t soff_a(const State& s, int t) {
-        return t < s.nt ? (uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ) : kOob;
+        return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ) : kOob);
     }
     __device__ static __forceinline__ uint32_t soff_b(const State& s, int t) {
-        return t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob;
+        return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob);
     }
     // Per-lane offset of chunk j.  FIRST: the chunk belongs to the last
     // physical K-tile (logical tile head-1), which may be ragged; chunks
@@ -245,30 +250,52 @@ struct Gemm {
             gload<0, LPT>(s, r, t);
     }
 
-    // RR B fragment: gather the EPC k-consecutive elements of one column.
-    __device__ static __forceinline__ i32x4 gather_b_rr(const uint8_t PG_LDS* bt, int n, int k0) {
-        i32x4 v;
+    // Layout RR B fragment (the tile is BK rows of BN N-contiguous
+    // elements).  16-bit and 8-bit types: two transposing reads, each giving
+    // the lane 4 (8) consecutive k of its column n; s.rrb[fn] is the lane's
+    // byte offset for step 0 and the first read, and the k advance of a step
+    // or of the second read is a whole number of rows (the swizzle repeats
+    // every rr_rows_per_read rows).  fp32: four single-element reads.
+    __device__ static __forceinline__ i32x4 read_b_rr(const State& s, const uint8_t PG_LDS* bt, int fn, int st) {
         if constexpr (SZ == 4) {
+            const int lane = s.tid & 63;
+            const int n = s.wn * WTN + fn * 32 + (lane & 31), k0 = (2 * st + (lane >> 5)) * EPC;
+            i32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = *(const int PG_LDS*)(bt + ((k0 + e) * BN + n) * 4);
-        } else if constexpr (SZ == 2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t lo = *(const uint16_t PG_LDS*)(bt + ((k0 + 2 * e) * BN + n) * 2);
-                uint32_t hi = *(const uint16_t PG_LDS*)(bt + ((k0 + 2 * e + 1) * BN + n) * 2);
-                v[e] = (int)(lo | (hi << 16));
-            }
+            return v;
         } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    w |= (uint32_t)(*(const uint8_t PG_LDS*)(bt + (k0 + 4 * e + b) * BN + n)) << (8 * b);
-                v[e] = (int)w;
+            typedef int i32x2v __attribute__((ext_vector_type(2)));
+            constexpr int RK = rr_rows_per_read(DT);            // k rows per transposing read
+            const uint8_t PG_LDS* p = bt + s.rrb[fn] + st * (2 * EPC) * RB_RR;
+            i32x2v lo, hi;
+            if constexpr (VARIANT == VAR_DIRECT) {
+                // With LDS-DMA writes in flight the compiler cannot tell that
+                // these reads touch another slot, and it would drain every
+                // outstanding load (vmcnt(0)) before each of them.  Issued as
+                // inline assembly they are invisible to its wait insertion:
+                // step() waits for them explicitly (lgkmcnt(0) at the start of
+                // the step that uses them).  The compiler's own lgkmcnt waits
+                // stay correct, only more conservative, because LDS operations
+                // complete in order.
+                const uint32_t a = (uint32_t)(uintptr_t)p;
+                if constexpr (SZ == 2) {
+                    asm volatile("ds_read_b64_tr_b16 %0, %2\n\tds_read_b64_tr_b16 %1, %2 offset:%3"
+                                 : "=&v"(lo), "=&v"(hi) : "v"(a), "i"(RK * RB_RR) : "memory");
+                } else {
+                    asm volatile("ds_read_b64_tr_b8 %0, %2\n\tds_read_b64_tr_b8 %1, %2 offset:%3"
+                                 : "=&v"(lo), "=&v"(hi) : "v"(a), "i"(RK * RB_RR) : "memory");
+                }
+            } else if constexpr (SZ == 2) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                lo = __builtin_bit_cast(i32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 PG_LDS*)p));
+                hi = __builtin_bit_cast(i32x2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 PG_LDS*)(p + RK * RB_RR)));
+            } else {
+                lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2v PG_LDS*)p);
+                hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2v PG_LDS*)(p + RK * RB_RR));
             }
+            return i32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        return v;
     }
 
     // Operand fragments of one MFMA step: FM A-side and FN B-side chunks.
@@ -279,24 +306,6 @@ struct Gemm {
 
     __device__ static __forceinline__ const uint8_t PG_LDS* slot_ptr(const uint8_t PG_LDS* smem, int slot) {
         return smem + slot * SLOT;
-    }
-
-    // Fragments of MFMA step `st` of the K-tile held in `slot`.
-    __device__ static __forceinline__ void read_frags(const State& s, const uint8_t PG_LDS* smem, int slot,
-                                                      int st, Frags& f) {
-        const uint8_t PG_LDS* as = slot_ptr(smem, slot);
-        const uint8_t PG_LDS* bs = as + A_BYTES;
-        const int lane = s.tid & 63;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            f.y[fm] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + fm * 32) * CPR * kChunk + s.rd[st]);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            if constexpr (RR)
-                f.x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
-            else
-                f.x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
-        }
     }
 
     // ---- the MFMA step schedule -------------------------------------------
@@ -326,7 +335,7 @@ struct Gemm {
         } else {
             const int fn = r - FM;
             if constexpr (RR)
-                f.x[fn] = gather_b_rr(bs, s.wn * WTN + fn * 32 + (lane & 31), (2 * st + (lane >> 5)) * EPC);
+                f.x[fn] = read_b_rr(s, bs, fn, st);
             else
                 f.x[fn] = *(const i32x4 PG_LDS*)(bs + (s.wn * WTN + fn * 32) * CPR * kChunk + s.rd[st]);
         }
@@ -360,6 +369,10 @@ struct Gemm {
                                                 Frags& nxt, int rd_slot, int rd_st, acc_t (&acc)[FM][FN],
                                                 int J0, int J1, int ld_kt, int ld_slot, i32x4 (&regs)[LPT]) {
         const int NL = J1 - J0;
+        if constexpr (RR && SZ != 4 && VARIANT == VAR_DIRECT) {
+            // the transposing reads of `cur` (inline assembly) have landed
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+        }
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
             const int fm = u / FN, fn = u % FN;
@@ -485,16 +498,35 @@ struct Gemm {
             s.kca[j] = (uint32_t)(c * EPC);
         }
         if constexpr (RR) {
-            // B tile is BK rows (k) of BN elements (n), unswizzled.
+            // B tile: BK rows (k) of BN elements (n); physical chunk pc of row
+            // r holds logical chunk pc ^ swz_rr(r).
 #pragma unroll
             for (int j = 0; j < LB; ++j) {
                 const int p = j * T + s.tid;
-                const int r = p / CPR_BRR, c = p % CPR_BRR;
+                const int r = p / CPR_BRR, c = (p % CPR_BRR) ^ swz_rr(DT, RB_RR, r);
                 const int cc = (n0 + c * EPC < args.N) ? c : 0;
                 s.offb[j] = (uint32_t)r * ldb_b + (uint32_t)(cc * EPC * SZ);
                 s.kcb[j] = (uint32_t)r;
             }
             s.kb_step = (uint32_t)BK * ldb_b;
+            if constexpr (SZ != 4) {
+                // Transposing reads: lane j of each 16-lane group g supplies
+                // the piece of row k at column n (see tile_layout.h).
+                const int h = lane >> 5, g = lane >> 4, jl = lane & 15;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    int k, n;
+                    if constexpr (SZ == 2) {
+                        k = 8 * h + jl / 4;
+                        n = s.wn * WTN + fn * 32 + 16 * (g & 1) + 4 * (jl & 3);
+                    } else {
+                        k = 16 * h + jl / 2;
+                        n = s.wn * WTN + fn * 32 + 16 * (g & 1) + 8 * (jl & 1);
+                    }
+                    const int c = n * SZ / kChunk, b = n * SZ % kChunk;
+                    s.rrb[fn] = (uint32_t)(k * RB_RR + (c ^ swz_rr(DT, RB_RR, k)) * kChunk + b);
+                }
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < LB; ++j) {

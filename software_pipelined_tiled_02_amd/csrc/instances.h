@@ -1,6 +1,6 @@
 // instances.h -- the kernel instances one translation unit compiles for one
-// input type: layout RC at every tile class, layout RR at the 128x128 and
-// 32x64 tiles, each at stages 1-4 and both load variants.
+// input type: both layouts at every tile class, each at stages 1-4 and both
+// load variants.
 #ifndef PIPEGEMM_INSTANCES_H
 #define PIPEGEMM_INSTANCES_H
 
@@ -25,7 +25,7 @@ inline void add_tile(KernelEntry* t, int& n) {
     t[n++] = entry<DT, LAYOUT, TC, 4, VAR_DIRECT>();
 }
 
-constexpr int kInstancesPerDtype = 5 * 8;
+constexpr int kInstancesPerDtype = 6 * 8;
 
 template <int DT>
 inline int fill_instances(KernelEntry* t) {
@@ -33,6 +33,7 @@ inline int fill_instances(KernelEntry* t) {
     add_tile<DT, LAYOUT_RC, TILE_L>(t, n);
     add_tile<DT, LAYOUT_RC, TILE_M>(t, n);
     add_tile<DT, LAYOUT_RC, TILE_T>(t, n);
+    add_tile<DT, LAYOUT_RR, TILE_L>(t, n);
     add_tile<DT, LAYOUT_RR, TILE_M>(t, n);
     add_tile<DT, LAYOUT_RR, TILE_T>(t, n);
     return n;

@@ -117,6 +117,29 @@ constexpr int swz(int cpr, int row) {
          : cpr == 4  ? ((row >> 2) & 3)
                      : 0;
 }
+// Row-major (K x N) B tile of layout RR: BK rows of N-contiguous data.  Its
+// MFMA fragments are read with gfx950's transposing LDS reads: within each
+// group of 16 lanes, every lane supplies the address of 8 bytes (4 fp16/bf16
+// or 8 int8 elements along N) from one of 4 (fp16/bf16) or 8 (int8)
+// consecutive K rows, and each lane receives the elements of one N column
+// from those rows -- the lane layout was measured with a probe:
+//   16-bit: out lane i, element e <- row-piece of lane 4e + i/4, element i%4
+//   8-bit:  out lane i, element e <- row-piece of lane 2e + i/8, element i%8.
+// Two such groups (32 lanes, 256 bytes) are served per clock and together
+// read 64 (16-bit) or 32 (8-bit) bytes from each of those rows.  The
+// swizzle below XORs the 16-byte chunk index of a row with a function of the
+// row so that these 4 or 8 row pieces land in different banks.  fp32 B
+// fragments are gathered element by element and are not swizzled.
+constexpr int rr_rows_per_read(int dt) { return dt == DT_I8 ? 8 : 4; }
+constexpr int rr_piece_bytes(int dt) { return dt == DT_I8 ? 32 : 64; }
+constexpr int swz_rr(int dt, int row_bytes, int k) {
+    return dt == DT_F32 ? 0
+         : ((k / (row_bytes >= 256 ? 1 : 256 / row_bytes))
+            % (rr_rows_per_read(dt) / (row_bytes >= 256 ? 1 : 256 / row_bytes) > 0
+                   ? rr_rows_per_read(dt) / (row_bytes >= 256 ? 1 : 256 / row_bytes) : 1))
+               * (rr_piece_bytes(dt) / kChunk);
+}
+
 // Physical chunk index (within the tile) of logical (row, chunk).
 constexpr int phys_chunk(int cpr, int row, int chunk) { return row * cpr + (chunk ^ swz(cpr, row)); }
 // Logical chunk that physical chunk p holds (the inverse of the above).

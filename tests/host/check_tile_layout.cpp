@@ -7,7 +7,8 @@
 //     served 16 consecutive lanes per clock, so within each 16-lane group
 //     the 16-byte bank groups (address / 16 mod 16) hit must all differ;
 //  3. without the swizzle the same read does conflict (so 2 is not vacuous);
-//  4. the K-tile order is a permutation with the ragged tile in the
+//  4. the transposing reads of layout RR's B tile are conflict-free;
+//  5. the K-tile order is a permutation with the ragged tile in the
 //     prologue, and every stage count adds the k-slices in one order.
 // Prints one line per chunks-per-row value; exits non-zero on failure.
 #include <cstdio>
@@ -61,6 +62,49 @@ int main() {
             for (int s = 1; s <= kMaxStages; ++s)
                 for (int v = 0; v < 2; ++v)
                     if (!instance_fits(dt, tc, s, v)) { std::printf("over budget %d %d %d %d\n", dt, tc, s, v); ++fail; }
+    // Layout RR: the transposing fragment reads of the N-contiguous B tile
+    // (lane addresses exactly as the kernel forms them) hit 64 different
+    // 4-byte banks in every group of 32 lanes, and the XOR keeps each row a
+    // permutation of its chunks; without the XOR they conflict.
+    int rr_fail = 0, rr_raw = 1;
+    for (int dt = 0; dt < 3; ++dt)
+        for (int tc = 0; tc < TILE_COUNT; ++tc) {
+            const int sz = in_size(dt), bn = tile_shape(tc).bn, rb = bn * sz, cpr_rr = rb / kChunk;
+            const int wtn = bn / tile_shape(tc).wn;
+            for (int k = 0; k < 256; ++k) {
+                const int x = swz_rr(dt, rb, k);
+                if (x < 0 || x >= cpr_rr || (cpr_rr & (cpr_rr - 1)) != 0) ++rr_fail;
+            }
+            for (int wn = 0; wn < tile_shape(tc).wn; ++wn)
+                for (int fn = 0; fn < wtn / 32; ++fn)
+                    for (int st = 0; st < 4; ++st)
+                        for (int r = 0; r < 2; ++r)
+                            for (int sw = 0; sw < 2; ++sw) {
+                                int worst = 1;
+                                for (int g0 = 0; g0 < 64; g0 += 32) {
+                                    int hits[64] = {0};
+                                    for (int l = g0; l < g0 + 32; ++l) {
+                                        const int h = l / 32, g = l / 16, j = l % 16;
+                                        const int nf = wn * wtn + fn * 32;
+                                        int k, n;
+                                        if (dt == DT_I8) { k = st * 32 + 16 * h + 8 * r + j / 2; n = nf + 16 * (g & 1) + 8 * (j & 1); }
+                                        else { k = st * 16 + 8 * h + 4 * r + j / 4; n = nf + 16 * (g & 1) + 4 * (j & 3); }
+                                        const int c = n * sz / kChunk, b = n * sz % kChunk;
+                                        const int addr = k * rb + ((sw ? c ^ swz_rr(dt, rb, k) : c) * kChunk) + b;
+                                        for (int w = 0; w < 2; ++w) {
+                                            const int bank = (addr / 4 + w) % 64;
+                                            if (++hits[bank] > worst) worst = hits[bank];
+                                        }
+                                    }
+                                }
+                                if (sw && worst != 1) ++rr_fail;
+                                if (!sw && worst > rr_raw) rr_raw = worst;
+                            }
+        }
+    std::printf("RR transposing reads: swizzled %s, unswizzled worst %d-way\n", rr_fail ? "CONFLICTS" : "conflict-free", rr_raw);
+    if (rr_raw == 1) ++rr_fail;
+    fail += rr_fail;
+
     // K-tile order: a permutation of the tiles whose last physical tile (the
     // ragged one) is logical tile head-1, and -- for the classes whose K-tile
     // halves at 3-4 stages -- the same sequence of MFMA k-slices (2 chunks

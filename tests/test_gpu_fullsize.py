@@ -23,6 +23,11 @@ WORKLOADS = {
     "bf16_skinny_8192x64x8192": (8192, 64, 8192, "bf16", "RC", "normal", 1.0, ALL_PAIRS),
     "bf16_8192x8192x8200": (8192, 8192, 8200, "bf16", "RC", "uniform", 1.0,
                             [(4, "direct"), (4, "reg"), (2, "direct"), (1, "direct")]),
+    # layout RR at the 256x256 tile (B fragments by transposing LDS reads)
+    "fp16_4096_rr": (4096, 4096, 4096, "f16", "RR", "normal", 1.0 / 64.0,
+                     [(2, "direct"), (2, "reg"), (4, "direct"), (1, "direct"), (3, "reg")]),
+    "int8_4096_rr": (4096, 4096, 4096, "i8", "RR", "int", 1.0,
+                     [(2, "direct"), (2, "reg"), (4, "direct"), (1, "reg")]),
 }
 
 

@@ -61,7 +61,7 @@ def test_alignment():
 
 def test_unsupported():
     U = binding.GEMM_ERR_UNSUPPORTED
-    assert q(layout="RR", tile="256x256")[0] == U
+    assert q(layout="RR", tile="256x256")[0] == binding.GEMM_OK   # every tile class has both layouts
     assert q(M=2 ** 31)[0] == U
     assert q(lda=2 ** 23, K=64)[0] == U           # 256 rows * 16 MiB > 2^31 B
 
@@ -100,6 +100,7 @@ def test_auto_tile_choice():
     assert q(M=8192, N=64, K=8192)[1]["tile"] == binding.GEMM_TILE_32x64
     assert q(M=2048, N=2048)[1]["tile"] == binding.GEMM_TILE_128x128  # 64 big tiles < 256 CUs
     assert q(dtype="f32", layout="RR", M=256, N=256, K=256)[1]["tile"] == binding.GEMM_TILE_32x64
+    assert q(layout="RR")[1]["tile"] == binding.GEMM_TILE_256x256
     info = q(M=8192, N=8192, K=8200, stages=4)[1]
     assert (info["c_tiles"], info["k_tiles"], info["k_tail"], info["block_k"]) == (1024, 257, 8, 32)
     assert info["grid"] == 256          # one workgroup per CU, four tiles each
