@@ -67,7 +67,7 @@ def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_02_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".h", ".hip")):
+        if name.endswith((".h", ".hip")) and name != "ceiling_probe.hip":   # the probe is no GEMM source
             h.update(name.encode())
             h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
@@ -88,6 +88,20 @@ def read_traffic(workload, stages, variant):
         return None
     key = "hbm_bytes_per_launch_S%d_%s" % (stages, variant)
     return float(vals[key]) if key in vals else None
+
+
+def measured_ceiling(dtype, bound):
+    """The chip's attainable rate for this dtype (MFMA loop fed from LDS with
+    random data) or for HBM (streaming read), from the committed output of
+    ceiling_probe; None if absent."""
+    path = os.path.join(ROOT, "profiles", "ceilings.txt")
+    if not os.path.exists(path):
+        return None
+    key = "hbm_read" if bound == "hbm" else "mfma_" + {"i8": "int8", "f16": "fp16", "bf16": "bf16", "f32": "fp32"}[dtype]
+    for line in open(path):
+        if line.startswith(key + ":"):
+            return float(line.split(":", 1)[1].split()[0])
+    return None
 
 
 def cpu_baseline(M, N, K, dtype, layout, dist, scale, target_s):
@@ -232,6 +246,11 @@ def main():
         roof = {"bound": "mfma", "achieved": round(r["tops"], 1), "peak": PEAK[dtype], "unit": unit,
                 "frac": round(r["tops"] / PEAK[dtype], 4)}
     roof["traffic"] = read_traffic(args.workload, best[0], best[1])
+    ceil = measured_ceiling(dtype, bound)
+    if ceil:
+        roof["measured_ceiling"] = {"value": ceil, "unit": roof["unit"], "frac": round(roof["achieved"] / ceil, 4),
+                                    "source": "profiles/ceilings.txt (ceiling_probe: MFMA fed from LDS with "
+                                              "random data / HBM streaming read)"}
     hot = None
     if bound == "hbm":
         # The same buffers every launch: A fits in the Infinity Cache, so this

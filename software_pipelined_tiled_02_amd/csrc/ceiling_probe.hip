@@ -1,0 +1,232 @@
+// ceiling_probe.hip -- attainable ceilings of one MI355X, to set beside the
+// datasheet peaks: the matrix-core rate per input type when the MFMAs are
+// fed from LDS the way the GEMM feeds them, and the HBM rate of a plain
+// streaming read and copy.  Standalone program (no GEMM code): prints one
+// "key: value" line per figure.
+//
+// MFMA ceiling.  One workgroup of 4 waves per CU; each wave keeps the GEMM's
+// 4 x 4 blocks of 32 x 32 accumulators and, per k-step, reads 8 operand
+// fragments (16 bytes per lane) from an LDS buffer of random values and
+// issues the 16 MFMAs of the step -- the GEMM's ratio of LDS reads to MFMAs,
+// without global memory traffic.  The data are random because the MFMA's
+// power draw, and with it the clock the chip holds, depends on the operand
+// bits; the effective clock is reported from s_memtime against the fixed
+// 100 MHz s_memrealtime.
+//
+// HBM ceiling.  A 1 GiB buffer (four times the Infinity Cache) read once with
+// 16-byte loads, each workgroup sweeping one contiguous block; and the same
+// buffer copied to a second one.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+#define LDSP __attribute__((address_space(3)))
+
+enum { I8 = 0, F16 = 1, BF16 = 2, F32 = 3 };
+
+template <int DT> struct Acc { typedef f32x16 type; };
+template <> struct Acc<I8> { typedef i32x16 type; };
+
+// acc += x * y over one 16-byte chunk per lane of each operand (fp32: four
+// k = 2 instructions, as in the GEMM).
+template <int DT>
+__device__ __forceinline__ typename Acc<DT>::type mma(i32x4 x, i32x4 y, typename Acc<DT>::type c) {
+    if constexpr (DT == BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    } else if constexpr (DT == F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+    } else if constexpr (DT == I8) {
+        return __builtin_amdgcn_mfma_i32_32x32x32_i8(x, y, c, 0, 0, 0);
+    } else {
+        const f32x4 xf = __builtin_bit_cast(f32x4, x), yf = __builtin_bit_cast(f32x4, y);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[0], yf[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[1], yf[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[2], yf[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(xf[3], yf[3], c, 0, 0, 0);
+        return c;
+    }
+}
+
+// k covered by one 16-byte chunk per lane and 32 x 32 block
+template <int DT> constexpr int chunk_k() { return DT == I8 ? 32 : DT == F32 ? 8 : 16; }
+
+constexpr int kLdsUnits = 4096;   // 64 KiB of 16-byte units
+
+// Random 16-byte unit i of workgroup b, with finite values of the type.
+__device__ __forceinline__ i32x4 random_unit(int dt, uint32_t i, uint32_t b) {
+    uint32_t x = i * 2654435761u + b * 40503u + 1u;
+    i32x4 v;
+    for (int e = 0; e < 4; ++e) {
+        x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+        uint32_t w = x;
+        if (dt == F16 || dt == BF16) w = (w & 0x83ff83ffu) | 0x38003800u;    // |v| in [0.5, 2)
+        if (dt == BF16) w = (x & 0x807f807fu) | 0x3f003f00u;
+        if (dt == F32) w = (w & 0x807fffffu) | 0x3f000000u;
+        v[e] = (int)w;
+    }
+    return v;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) mfma_ceiling(int iters, int* out, unsigned long long* clk) {
+    typedef typename Acc<DT>::type acc_t;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsUnits * 16];
+    i32x4 LDSP* lds = (i32x4 LDSP*)lds_raw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < kLdsUnits; i += 256) lds[i] = random_unit(DT, (uint32_t)i, blockIdx.x);
+    __syncthreads();
+    const unsigned long long t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
+    acc_t acc[4][4];
+    for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b)
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0;
+    for (int it = 0; it < iters; ++it) {
+        i32x4 x[4], y[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            // unit index < 64 * 64 = kLdsUnits
+            x[a] = lds[((it * 8 + a) & 63) * 64 + lane];
+            y[a] = lds[((it * 8 + 4 + a) & 63) * 64 + lane];
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = mma<DT>(x[b], y[a], acc[a][b]);
+    }
+    const unsigned long long t1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
+    int s = 0;
+    for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b) {
+            const i32x16 ai = __builtin_bit_cast(i32x16, acc[a][b]);   // whole-vector cast, then index
+            s ^= ai[0] ^ ai[15];
+        }
+    out[blockIdx.x * 256 + tid] = s;
+    if (tid == 0) {
+        clk[blockIdx.x * 2] = t1 - t0;
+        clk[blockIdx.x * 2 + 1] = r1 - r0;
+    }
+}
+
+// Each workgroup reads (and for the copy, writes) one contiguous block of
+// `per_wg` bytes, 4 x 16 bytes per lane per pass.
+__global__ void __launch_bounds__(256) hbm_read(const i32x4* __restrict__ src, uint64_t per_wg, int* out) {
+    const i32x4* p = src + (uint64_t)blockIdx.x * (per_wg / 16);
+    i32x4 acc = {0, 0, 0, 0};
+    for (uint64_t u = threadIdx.x; u < per_wg / 16; u += 4 * 256) {
+        i32x4 v0 = p[u], v1 = p[u + 256], v2 = p[u + 512], v3 = p[u + 768];
+        acc ^= v0 ^ v1 ^ v2 ^ v3;
+    }
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x5a5a5a5a) out[threadIdx.x] = acc[0];
+}
+
+__global__ void __launch_bounds__(256) hbm_copy(const i32x4* __restrict__ src, i32x4* __restrict__ dst, uint64_t per_wg) {
+    const uint64_t base = (uint64_t)blockIdx.x * (per_wg / 16);
+    for (uint64_t u = threadIdx.x; u < per_wg / 16; u += 4 * 256) {
+        i32x4 v0 = src[base + u], v1 = src[base + u + 256], v2 = src[base + u + 512], v3 = src[base + u + 768];
+        dst[base + u] = v0;
+        dst[base + u + 256] = v1;
+        dst[base + u + 512] = v2;
+        dst[base + u + 768] = v3;
+    }
+}
+
+#define CHECK(x)                                                                 \
+    do {                                                                         \
+        hipError_t e_ = (x);                                                     \
+        if (e_ != hipSuccess) {                                                  \
+            std::fprintf(stderr, "%s: %s\n", #x, hipGetErrorString(e_));         \
+            return 1;                                                            \
+        }                                                                        \
+    } while (0)
+
+template <int DT>
+int run_mfma(const char* name, double peak, int cus) {
+    int* out;
+    unsigned long long* clk;
+    CHECK(hipMalloc(&out, (size_t)cus * 256 * sizeof(int)));
+    CHECK(hipMalloc(&clk, (size_t)cus * 2 * sizeof(unsigned long long)));
+    const int iters = DT == F32 ? 2000 : 8000;
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(mfma_ceiling<DT>, dim3(cus), dim3(256), 0, 0, iters, out, clk);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    const int reps = 5;
+    for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(mfma_ceiling<DT>, dim3(cus), dim3(256), 0, 0, iters, out, clk);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    ms /= reps;
+    std::vector<unsigned long long> h((size_t)cus * 2);
+    CHECK(hipMemcpy(h.data(), clk, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+    double cyc = 0, rt = 0;
+    for (int b = 0; b < cus; ++b) {
+        cyc += (double)h[2 * b];
+        rt += (double)h[2 * b + 1];
+    }
+    const double ghz = cyc / (rt / 100e6) / 1e9;
+    // per wave and iteration: 16 blocks of 32 x 32 x chunk_k multiply-adds
+    const double ops = 2.0 * 16 * 32 * 32 * chunk_k<DT>() * 4 * (double)cus * iters;
+    const double t = ops / (ms * 1e-3) / 1e12;
+    std::printf("mfma_%s: %.1f %s, effective clock %.3f GHz, %.1f%% of the %.1f datasheet peak\n", name, t,
+                DT == I8 ? "TOP/s" : "TFLOP/s", ghz, 100.0 * t / peak, peak);
+    CHECK(hipFree(out));
+    CHECK(hipFree(clk));
+    return 0;
+}
+
+}  // namespace
+
+int main() {
+    int dev = 0, cus = 0;
+    CHECK(hipGetDevice(&dev));
+    CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    std::printf("compute_units: %d\n", cus);
+    if (run_mfma<I8>("int8", 5033.2, cus) || run_mfma<F16>("fp16", 2516.6, cus) ||
+        run_mfma<BF16>("bf16", 2516.6, cus) || run_mfma<F32>("fp32", 157.3, cus))
+        return 1;
+
+    const uint64_t bytes = (uint64_t)1 << 30;
+    const int wgs = 4096;                       // 256 KiB per workgroup
+    const uint64_t per_wg = bytes / wgs;        // a multiple of 4 * 256 * 16 bytes
+    i32x4 *src, *dst;
+    int* out;
+    CHECK(hipMalloc(&src, bytes));
+    CHECK(hipMalloc(&dst, bytes));
+    CHECK(hipMalloc(&out, 256 * sizeof(int)));
+    CHECK(hipMemset(src, 1, bytes));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    float ms;
+    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(hbm_read, dim3(wgs), dim3(256), 0, 0, src, per_wg, out);
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 10; ++r) hipLaunchKernelGGL(hbm_read, dim3(wgs), dim3(256), 0, 0, src, per_wg, out);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("hbm_read: %.1f GB/s (1 GiB, 16-byte loads)\n", (double)bytes * 10 / (ms * 1e-3) / 1e9);
+    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(hbm_copy, dim3(wgs), dim3(256), 0, 0, src, dst, per_wg);
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 10; ++r) hipLaunchKernelGGL(hbm_copy, dim3(wgs), dim3(256), 0, 0, src, dst, per_wg);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("hbm_copy: %.1f GB/s (read + write bytes, 1 GiB each way)\n", 2.0 * bytes * 10 / (ms * 1e-3) / 1e9);
+    CHECK(hipFree(src));
+    CHECK(hipFree(dst));
+    CHECK(hipFree(out));
+    return 0;
+}

@@ -47,3 +47,13 @@ def test_traffic_is_read_only_for_the_current_kernel_sources(tmp_path, monkeypat
 def test_kernel_hash_covers_the_kernel_sources():
     h1 = bench.kernel_source_hash()
     assert len(h1) == 16 and h1 == bench.kernel_source_hash()
+
+
+def test_measured_ceiling_is_read_from_the_probe_output():
+    """The committed ceiling_probe output gives one attainable rate per dtype
+    and one for HBM, each below its datasheet peak."""
+    for dt in ("i8", "f16", "bf16", "f32"):
+        c = bench.measured_ceiling(dt, "mfma")
+        assert c is not None and 0 < c <= bench.PEAK[dt], (dt, c)
+    h = bench.measured_ceiling("bf16", "hbm")
+    assert h is not None and 0 < h <= bench.HBM_PEAK_GBS
