@@ -2,8 +2,10 @@
 
 Each translation unit under csrc/ is compiled on its own (in parallel) and
 the objects are linked into software_pipelined_tiled_02_amd/libpipegemm.so.
-The standalone ceiling probe (csrc/ceiling_probe.hip: MFMA and HBM rates of
-the chip, no GEMM code) is built beside it as `ceiling_probe`.
+Two standalone measurement programs are built beside it: `ceiling_probe`
+(csrc/ceiling_probe.hip: MFMA and HBM rates of the chip, no GEMM code) and
+`lds_layout_probe` (csrc/lds_layout_probe.hip: LDS bank conflicts of the
+fragment reads under three tile layouts).
 """
 import os
 import subprocess
@@ -14,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpipegemm.so")
-PROBE = os.path.join(HERE, "ceiling_probe")
+PROBES = ["ceiling_probe", "lds_layout_probe"]
 SOURCES = ["abi.hip", "kernels_i8.hip", "kernels_f16.hip", "kernels_bf16.hip", "kernels_f32.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,9 +54,11 @@ def build(jobs=None, verbose=False):
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    tmp = PROBE + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, "ceiling_probe.hip"), "-o", tmp], check=True)
-    os.replace(tmp, PROBE)
+    for name in PROBES:
+        exe = os.path.join(HERE, name)
+        tmp = exe + ".tmp%d" % os.getpid()
+        subprocess.run([HIPCC, *FLAGS, os.path.join(CSRC, name + ".hip"), "-o", tmp], check=True)
+        os.replace(tmp, exe)
     return LIB
 
 
