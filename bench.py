@@ -134,6 +134,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--pairs", default="all", help="comma list like 3:direct,2:reg, or all")
+    ap.add_argument("--tile", default="auto", help="tile class: auto, 256x256, 256x256w8, 128x128, 32x64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -159,6 +160,7 @@ def main():
         pairs = [(int(p.split(":")[0]), p.split(":")[1]) for p in args.pairs.split(",")]
 
     g = binding.Gemm(0)
+    g.set_tile(args.tile)
     a, b = inputs.make_operands(M, N, K, dtype, layout, dist, seed=0, scale=scale)
     a, b = a.cuda(), b.cuda()
     out_dt = inputs.OUT_TORCH_DTYPES[dtype]
@@ -235,7 +237,7 @@ def main():
 
     best = min(results, key=lambda p: results[p]["mean_us"])
     r = results[best]
-    _, info = binding.gemm_query(M, N, K, dtype, layout, best[0], best[1])
+    _, info = binding.gemm_query(M, N, K, dtype, layout, best[0], best[1], tile=args.tile)
     unit = "TOP/s" if dtype == "i8" else "TFLOP/s"
     if bound == "hbm":
         value, vunit = r["gbs"], "GB/s"

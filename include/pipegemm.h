@@ -79,10 +79,13 @@ enum {
                                   failure); see gemm_last_hip_error */
 };
 
-/* Tile classes selectable with gemm_set_tile (GEMM_TILE_AUTO lets the
- * library choose the largest tile that still gives at least one workgroup
- * per compute unit). */
-enum { GEMM_TILE_AUTO = -1, GEMM_TILE_256x256 = 0, GEMM_TILE_128x128 = 1, GEMM_TILE_32x64 = 2 };
+/* Tile classes selectable with gemm_set_tile.  GEMM_TILE_256x256_W8 is the
+ * 256x256 tile run by 8 waves (2 per SIMD) instead of 4; it is never chosen
+ * automatically (its register-staged instances spill a few registers).
+ * GEMM_TILE_AUTO lets the library choose the largest of the 4-wave tiles
+ * that still gives at least one workgroup per compute unit. */
+enum { GEMM_TILE_AUTO = -1, GEMM_TILE_256x256 = 0, GEMM_TILE_128x128 = 1, GEMM_TILE_32x64 = 2,
+       GEMM_TILE_256x256_W8 = 3 };
 
 typedef struct gemm_handle_s *gemm_handle_t;
 
@@ -100,7 +103,7 @@ typedef struct {
     int64_t grid;            /* workgroups launched */
     int64_t k_tiles;         /* ceil(K / block_k) */
     int32_t k_tail;          /* K mod block_k; 0 means no ragged last tile */
-    int32_t c_tiles;         /* C tiles; above grid when each workgroup of the
+    int32_t c_tiles;         /* C tiles; above grid when each workgroup of a
                                 256x256 tile computes several in turn (then
                                 grid = one workgroup per CU) */
 } gemm_config_info_t;

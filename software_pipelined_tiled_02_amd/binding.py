@@ -15,13 +15,13 @@ GEMM_I8, GEMM_F16, GEMM_BF16, GEMM_F32 = 0, 1, 2, 3
 GEMM_LAYOUT_RR, GEMM_LAYOUT_RC = 0, 1
 GEMM_VARIANT_REG, GEMM_VARIANT_DIRECT = 0, 1
 GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_ALIGNMENT, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP = 0, 1, 2, 3, 4
-GEMM_TILE_AUTO, GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_32x64 = -1, 0, 1, 2
+GEMM_TILE_AUTO, GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_32x64, GEMM_TILE_256x256_W8 = -1, 0, 1, 2, 3
 
 DTYPES = {"i8": GEMM_I8, "f16": GEMM_F16, "bf16": GEMM_BF16, "f32": GEMM_F32}
 LAYOUTS = {"RR": GEMM_LAYOUT_RR, "RC": GEMM_LAYOUT_RC}
 VARIANTS = {"reg": GEMM_VARIANT_REG, "direct": GEMM_VARIANT_DIRECT}
 TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_TILE_128x128,
-         "32x64": GEMM_TILE_32x64}
+         "32x64": GEMM_TILE_32x64, "256x256w8": GEMM_TILE_256x256_W8}
 
 # C functions exported by the library (the names include/pipegemm.h declares)
 EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",

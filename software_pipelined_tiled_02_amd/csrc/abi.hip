@@ -67,6 +67,9 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
 
     // Tile class: the largest whose grid still gives every CU a workgroup.
+    // (The 8-wave 256x256 tile is only taken on request: with operands
+    // streamed from HBM it measured level with the 4-wave one on 8192^2,
+    // behind it on 4096^3, and ahead only with cache-resident operands.)
     int tc = tile;
     if (tc == GEMM_TILE_AUTO) {
         tc = pg::TILE_T;
@@ -106,12 +109,12 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.tiles_in_flight = pg::tiles_in_flight(variant, stages);
     in.lds_bytes = pg::lds_bytes(dtype, tc, stages, variant);
     in.loads_per_tile = pg::loads_a(dtype, tc, stages) + pg::loads_b(dtype, tc, stages);
-    // The 256x256 tile runs one workgroup per CU (its LDS ring and
+    // The 256x256 tiles run one workgroup per CU (their LDS ring and
     // registers allow no second one); with more tiles than CUs, a grid of
     // one workgroup per CU loops over the tiles, so that one tile's C stores
     // overlap the next tile's first loads.
     in.c_tiles = (int32_t)(tm * tn);
-    in.grid = (tc == pg::TILE_L && tm * tn > num_cus && num_cus % 8 == 0) ? num_cus : tm * tn;
+    in.grid = ((tc == pg::TILE_L || tc == pg::TILE_W) && tm * tn > num_cus && num_cus % 8 == 0) ? num_cus : tm * tn;
     in.k_tiles = ceil_div(K, bk);
     in.k_tail = (int32_t)(K % bk);
     plan->tile = tc;

@@ -479,9 +479,9 @@ struct Gemm {
         // row-strided reads of A pile onto the same HBM channels (measured on
         // the skinny 8192x64x8192 shape: 4.0 -> 4.5 TB/s).  Within an XCD the
         // tiles keep a common K position, so they still share B in its L2.
-        // The 256x256 tile keeps the plain order: its bands share A and B
+        // The 256x256 tiles keep the plain order: their bands share A and B
         // across each XCD's tiles and gain nothing from it.
-        s.rot = (TC != TILE_L && s.nbody > 0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)s.nbody) : 0;
+        s.rot = (BM < 256 && s.nbody > 0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)s.nbody) : 0;
         const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
         const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
                               : (const uint8_t*)args.B + (int64_t)n0 * args.ldb * SZ;

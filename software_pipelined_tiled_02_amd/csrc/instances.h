@@ -25,15 +25,17 @@ inline void add_tile(KernelEntry* t, int& n) {
     t[n++] = entry<DT, LAYOUT, TC, 4, VAR_DIRECT>();
 }
 
-constexpr int kInstancesPerDtype = 6 * 8;
+constexpr int kInstancesPerDtype = 8 * 8;
 
 template <int DT>
 inline int fill_instances(KernelEntry* t) {
     int n = 0;
     add_tile<DT, LAYOUT_RC, TILE_L>(t, n);
+    add_tile<DT, LAYOUT_RC, TILE_W>(t, n);
     add_tile<DT, LAYOUT_RC, TILE_M>(t, n);
     add_tile<DT, LAYOUT_RC, TILE_T>(t, n);
     add_tile<DT, LAYOUT_RR, TILE_L>(t, n);
+    add_tile<DT, LAYOUT_RR, TILE_W>(t, n);
     add_tile<DT, LAYOUT_RR, TILE_M>(t, n);
     add_tile<DT, LAYOUT_RR, TILE_T>(t, n);
     return n;

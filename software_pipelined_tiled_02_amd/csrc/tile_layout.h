@@ -34,7 +34,7 @@ namespace pg {
 enum DType : int { DT_I8 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
 enum Layout : int { LAYOUT_RR = 0, LAYOUT_RC = 1 };
 enum Variant : int { VAR_REG = 0, VAR_DIRECT = 1 };
-enum TileClass : int { TILE_L = 0, TILE_M = 1, TILE_T = 2, TILE_COUNT = 3 };
+enum TileClass : int { TILE_L = 0, TILE_M = 1, TILE_T = 2, TILE_W = 3, TILE_COUNT = 4 };
 
 constexpr int kMaxStages = 4;
 constexpr int kLdsBudget = 160 * 1024;   // bytes of LDS per CU on gfx950
@@ -46,10 +46,13 @@ constexpr int out_size(int dt) { return dt == DT_I8 ? 4 : (dt == DT_F32 ? 4 : 2)
 constexpr int epc(int dt) { return kChunk / in_size(dt); }
 
 // Workgroup tile and wave grid of each class.  Each wave owns a
-// (bm/wm) x (bn/wn) block of C made of 32x32 MFMA blocks.
+// (bm/wm) x (bn/wn) block of C made of 32x32 MFMA blocks.  TILE_W is the
+// 256x256 tile with 8 waves (2 per SIMD, 128x64 each): while one wave of a
+// SIMD waits (on its loads, on the barrier), the other can issue MFMAs.
 struct TileShape { int bm, bn, wm, wn; };
 constexpr TileShape tile_shape(int tc) {
     return tc == TILE_L ? TileShape{256, 256, 2, 2}
+         : tc == TILE_W ? TileShape{256, 256, 2, 4}
          : tc == TILE_M ? TileShape{128, 128, 2, 2}
                         : TileShape{32, 64, 1, 2};
 }
@@ -58,7 +61,7 @@ constexpr TileShape tile_shape(int tc) {
 // at 3-4 stages so that the ring stays inside the LDS budget (the remedy the
 // skill gives for a buffer over the cliff: halve BK).
 constexpr int cpr_k(int tc, int stages) {
-    return tc == TILE_L ? (stages <= 2 ? 8 : 4) : tc == TILE_M ? 8 : 16;
+    return (tc == TILE_L || tc == TILE_W) ? (stages <= 2 ? 8 : 4) : tc == TILE_M ? 8 : 16;
 }
 constexpr int block_k(int dt, int tc, int stages) { return cpr_k(tc, stages) * epc(dt); }
 

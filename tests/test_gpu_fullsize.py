@@ -93,14 +93,15 @@ PERSISTENT = {
 }
 
 
+@pytest.mark.parametrize("tile", ["256x256", "256x256w8"])
 @pytest.mark.parametrize("name", list(PERSISTENT))
-def test_tile_loop_with_edges(name):
+def test_tile_loop_with_edges(name, tile):
     M, N, K, dtype, dist, scale = PERSISTENT[name]
-    print("workload:", name, flush=True)
+    print("workload:", name, tile, flush=True)
     gg = binding.Gemm(0)
     try:
-        gg.set_tile("256x256")
-        _, info = binding.gemm_query(M, N, K, dtype, "RC", 2, "direct", tile="256x256")
+        gg.set_tile(tile)
+        _, info = binding.gemm_query(M, N, K, dtype, "RC", 2, "direct", tile=tile)
         assert info["c_tiles"] > info["grid"] == 256, info
         a, b = inputs.make_operands(M, N, K, dtype, "RC", dist, seed=3, scale=scale)
         rows, cols = sample_points(M, N, 3000, seed=4)

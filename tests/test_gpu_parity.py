@@ -22,8 +22,8 @@ DTYPES = ("i8", "f16", "bf16", "f32")
 STAGES = (1, 2, 3, 4)
 VARIANTS = ("reg", "direct")
 # (layout, tile) pairs the library builds
-LAYOUT_TILES = [("RC", "256x256"), ("RC", "128x128"), ("RC", "32x64"),
-                ("RR", "256x256"), ("RR", "128x128"), ("RR", "32x64")]
+LAYOUT_TILES = [("RC", "256x256"), ("RC", "256x256w8"), ("RC", "128x128"), ("RC", "32x64"),
+                ("RR", "256x256"), ("RR", "256x256w8"), ("RR", "128x128"), ("RR", "32x64")]
 DIST = {"i8": "int", "f16": "normal", "bf16": "uniform", "f32": "uniform"}
 # K with a ragged last tile for every K-tile size of the dtype
 SMALL_K = {"i8": 400, "f16": 200, "bf16": 200, "f32": 100}

@@ -91,6 +91,11 @@ def test_large_tile_budget(dtype, bk2, bk4):
             # fp16/bf16, rows padded by 32 B)
             strips = 4 * 32 * (128 * 4 + 16 if dtype in ("i8", "f32") else 128 * 2 + 32)
             assert info["lds_bytes"] == max(ring, strips) <= 160 * 1024
+            # the 8-wave 256x256 tile: the same ring, 8 strips of 64-column blocks
+            rc, w8 = q(dtype=dtype, stages=stages, variant=variant, tile="256x256w8")
+            assert rc == binding.GEMM_OK and w8["threads"] == 512 and w8["block_k"] == bk
+            strips8 = 8 * 32 * (64 * 4 + 16 if dtype in ("i8", "f32") else 64 * 2 + 32)
+            assert w8["lds_bytes"] == max(ring, strips8) <= 160 * 1024
             assert info["reg_sets"] == (0 if variant == "direct" else max(1, stages - 1))
             assert info["tiles_in_flight"] == (stages - 1 if variant == "direct" else max(1, stages - 1))
 
@@ -102,6 +107,9 @@ def test_auto_tile_choice():
     assert q(dtype="f32", layout="RR", M=256, N=256, K=256)[1]["tile"] == binding.GEMM_TILE_32x64
     assert q(layout="RR")[1]["tile"] == binding.GEMM_TILE_256x256
     info = q(M=8192, N=8192, K=8200, stages=4)[1]
+    assert info["tile"] == binding.GEMM_TILE_256x256 and info["threads"] == 256
+    w8 = q(M=8192, N=8192, K=8200, stages=4, tile="256x256w8")[1]
+    assert (w8["tile"], w8["threads"], w8["grid"]) == (binding.GEMM_TILE_256x256_W8, 512, 256)
     assert (info["c_tiles"], info["k_tiles"], info["k_tail"], info["block_k"]) == (1024, 257, 8, 32)
     assert info["grid"] == 256          # one workgroup per CU, four tiles each
     assert q()[1]["grid"] == q()[1]["c_tiles"] == 256
