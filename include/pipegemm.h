@@ -26,6 +26,20 @@
  *   GEMM_LAYOUT_RC: B column-major K x N:  B(k,j) = B[j*ldb + k], ldb >= K.
  *   C is always row-major M x N:  C(i,j) = C[i*ldc + j], ldc >= N.
  *
+ * Alignment:
+ *   C: 16-byte aligned, ldc a multiple of 4 elements.  Layout RR: N a
+ *     multiple of 16 bytes worth of elements.
+ *   A and B, GEMM_VARIANT_DIRECT: 16-byte aligned, lda and ldb times the
+ *     element size multiples of 16 bytes, K a multiple of 16 bytes worth of
+ *     elements (its copies move whole aligned 16-byte chunks).
+ *   A and B, GEMM_VARIANT_REG: aligned to their element size; any K, lda and
+ *     ldb.  When K is not a multiple of 16 bytes worth of elements the chunk
+ *     holding column K-1 of each row is read in exact 8/4/2/1-byte pieces
+ *     (the bounds-checked fallback for the last tile that "pipeline-gpu-kernel"
+ *     names under its pitfalls, cp.async boundary handling): no byte past
+ *     column K-1 of a row is read.  Rows and pointers that are not 16-byte
+ *     aligned are read with unaligned 16-byte loads.
+ *
  * Pipeline depth and load path:
  *   stages in [1, 4].
  *   GEMM_VARIANT_DIRECT: global -> LDS copies that bypass registers (the
@@ -69,10 +83,9 @@ enum {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = 1,  /* NULL handle/pointer, negative size, bad enum,
                                   leading dimension too small, stages not in [1,4] */
-    GEMM_ERR_ALIGNMENT = 2,    /* a base pointer not 16-byte aligned, lda/ldb/ldc
-                                  times the element size not a multiple of 16 B,
-                                  or K (and N for layout RR) not a multiple of
-                                  16 B worth of elements */
+    GEMM_ERR_ALIGNMENT = 2,    /* an alignment rule above is broken: C's, RR's N,
+                                  A/B not element-aligned, or (direct variant
+                                  only) A/B rows or K not whole 16-byte chunks */
     GEMM_ERR_UNSUPPORTED = 3,  /* no kernel instance fits the LDS budget, or an
                                   operand tile row span exceeds 2^31 bytes */
     GEMM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch

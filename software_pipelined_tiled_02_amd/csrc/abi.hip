@@ -25,6 +25,7 @@ constexpr int kDefaultCus = 256;  // MI355X; used when no device is at hand
 struct Plan {
     gemm_config_info_t info;
     int tile;
+    int kernel_variant;   // pg::Variant of the instance launched
     int64_t tiles_m, tiles_n;
 };
 
@@ -59,10 +60,16 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (lda < 0 || ldb < 0 || ldc < 0) return GEMM_ERR_INVALID_ARG;
 
     const int sz = pg::in_size(dtype), osz = pg::out_size(dtype), epc = pg::epc(dtype);
-    if (reads_a && (!aligned16(A) || (lda * sz) % 16 != 0)) return GEMM_ERR_ALIGNMENT;
-    if (reads_b && (!aligned16(B) || (ldb * sz) % 16 != 0)) return GEMM_ERR_ALIGNMENT;
+    // Operands: element-aligned always; 16-byte aligned rows (base, ld and K
+    // whole 16-byte chunks) for the direct-to-LDS variant, whose loads write
+    // LDS in whole 16-byte chunks.  The register-staged variant takes any K
+    // and leading dimension.
+    if (reads_a && (uintptr_t)A % sz != 0) return GEMM_ERR_ALIGNMENT;
+    if (reads_b && (uintptr_t)B % sz != 0) return GEMM_ERR_ALIGNMENT;
+    const bool rows16 = (!reads_a || (aligned16(A) && (lda * sz) % 16 == 0)) &&
+                        (!reads_b || (aligned16(B) && (ldb * sz) % 16 == 0)) && K % epc == 0;
+    if (!rows16 && variant == GEMM_VARIANT_DIRECT) return GEMM_ERR_ALIGNMENT;
     if (has_c && (!aligned16(C) || ldc % 4 != 0)) return GEMM_ERR_ALIGNMENT;
-    if (K % epc != 0) return GEMM_ERR_ALIGNMENT;
     if (layout == GEMM_LAYOUT_RR && N % epc != 0) return GEMM_ERR_ALIGNMENT;
     if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
 
@@ -118,6 +125,10 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.k_tiles = ceil_div(K, bk);
     in.k_tail = (int32_t)(K % bk);
     plan->tile = tc;
+    // A K that is not a multiple of 16 bytes reads its partial chunk with
+    // exact-size loads, in instances of their own; the other instances are
+    // not touched by it.
+    plan->kernel_variant = (variant == GEMM_VARIANT_REG && K % epc != 0) ? (int)pg::VAR_REG_KTAIL : variant;
     plan->tiles_m = tm;
     plan->tiles_n = tn;
     (void)osz;
@@ -125,7 +136,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
 }
 
 struct Registry {
-    const void* fn[4][2][pg::TILE_COUNT][pg::kMaxStages + 1][2];
+    const void* fn[4][2][pg::TILE_COUNT][pg::kMaxStages + 1][3];
     Registry() {
         memset(fn, 0, sizeof fn);
         const pg::KernelEntry* (*parts[4])(int*) = {pg::kernels_i8, pg::kernels_f16, pg::kernels_bf16,
@@ -204,7 +215,7 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int la
     if (rc != GEMM_OK) return rc;
     if (plan.info.grid == 0) return GEMM_OK;
 
-    const void* fn = registry().fn[dtype][layout][plan.tile][stages][variant];
+    const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
     if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;
 
     pg::GemmArgs args;

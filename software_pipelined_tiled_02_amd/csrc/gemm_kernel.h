@@ -219,6 +219,20 @@ struct Gemm {
     template <int J0, int J1, bool FIRST = false>
     __device__ static __forceinline__ void gload(const State& s, i32x4 (&r)[LPT], int kt) {
         const uint32_t sa = soff_a(s, kt), sb = soff_b(s, kt);
+        if constexpr (FIRST && VARIANT == VAR_REG_KTAIL) {
+            // K is not a multiple of EPC: the chunk holding column K-1 is
+            // partly past K.
+#pragma unroll
+            for (int j = J0; j < J1; ++j) {
+                if (j < LA)
+                    r[j] = load_k_tail(s, s.ra, s.offa[j], s.kca[j], sa);
+                else if constexpr (RR)
+                    r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, voff_b<true>(s, j - LA), sb, 0);
+                else
+                    r[j] = load_k_tail(s, s.rb, s.offb[j - LA], s.kcb[j - LA], sb);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = J0; j < J1; ++j) {
             if (j < LA)
@@ -226,6 +240,38 @@ struct Gemm {
             else
                 r[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, voff_b<FIRST>(s, j - LA), sb, 0);
         }
+    }
+
+    // One K-contiguous chunk of the last physical K-tile when K is not a
+    // multiple of EPC: `rem` of its elements lie before K.  rem <= 0 gives
+    // zeros, rem >= EPC the whole chunk.  A partial chunk's vb = rem * SZ
+    // bytes are read in pieces of 8, 4, 2 and 1 bytes following the binary
+    // digits of vb (a piece that is not there takes the out-of-range offset
+    // and reads 0), so no byte past K is read and no read passes the end of
+    // the matrix; the bytes after vb stay zero.
+    __device__ static __forceinline__ i32x4 load_k_tail(const State& s, __amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                                       uint32_t kc, uint32_t soff) {
+        int rem = s.K - (int)(kc + (uint32_t)(s.nt - 1) * BK);
+        // `rem` is the same for every tile; kept opaque, so the compiler forms
+        // the offsets below here instead of hoisting them all out of the tile
+        // loop into scalar registers (which then spill).
+        asm volatile("" : "+v"(rem));
+        const uint32_t vb = (rem > 0 && rem < EPC) ? (uint32_t)(rem * SZ) : 0u;
+        i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, rem >= EPC ? off : kOob, soff, 0);
+        const i32x2 p8 = __builtin_amdgcn_raw_buffer_load_b64(rs, (vb & 8) ? off : kOob, soff, 0);
+        const int p4 = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (vb & 4) ? off + (vb & 8) : kOob, soff, 0);
+        uint32_t t = 0;                                     // the 2- and 1-byte pieces: one dword
+        if constexpr (SZ <= 2)
+            t = __builtin_amdgcn_raw_buffer_load_b16(rs, (vb & 2) ? off + (vb & 12) : kOob, soff, 0);
+        if constexpr (SZ == 1)
+            t |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, (vb & 1) ? off + (vb & 14) : kOob, soff, 0)
+                 << (8 * (vb & 2));
+        const uint32_t d4 = (vb & 8) >> 2, dt = (vb & 12) >> 2;   // dwords the 4-byte piece and `t` land in
+        v[0] |= p8[0] | (d4 == 0 ? p4 : 0) | (dt == 0 ? (int)t : 0);
+        v[1] |= p8[1] | (dt == 1 ? (int)t : 0);
+        v[2] |= (d4 == 2 ? p4 : 0) | (dt == 2 ? (int)t : 0);
+        v[3] |= (dt == 3 ? (int)t : 0);
+        return v;
     }
     __device__ static __forceinline__ void swrite(const State& s, uint8_t PG_LDS* smem, const i32x4 (&r)[LPT], int slot) {
         i32x4 PG_LDS* base = (i32x4 PG_LDS*)(smem + slot * SLOT);

@@ -1,6 +1,7 @@
 // instances.h -- the kernel instances one translation unit compiles for one
 // input type: both layouts at every tile class, each at stages 1-4 and both
-// load variants.
+// load variants, plus the register-staged variant's instances for a K that
+// is not a multiple of 16 bytes.
 #ifndef PIPEGEMM_INSTANCES_H
 #define PIPEGEMM_INSTANCES_H
 
@@ -23,9 +24,13 @@ inline void add_tile(KernelEntry* t, int& n) {
     t[n++] = entry<DT, LAYOUT, TC, 2, VAR_DIRECT>();
     t[n++] = entry<DT, LAYOUT, TC, 3, VAR_DIRECT>();
     t[n++] = entry<DT, LAYOUT, TC, 4, VAR_DIRECT>();
+    t[n++] = entry<DT, LAYOUT, TC, 1, VAR_REG_KTAIL>();
+    t[n++] = entry<DT, LAYOUT, TC, 2, VAR_REG_KTAIL>();
+    t[n++] = entry<DT, LAYOUT, TC, 3, VAR_REG_KTAIL>();
+    t[n++] = entry<DT, LAYOUT, TC, 4, VAR_REG_KTAIL>();
 }
 
-constexpr int kInstancesPerDtype = 8 * 8;
+constexpr int kInstancesPerDtype = 8 * 12;
 
 template <int DT>
 inline int fill_instances(KernelEntry* t) {

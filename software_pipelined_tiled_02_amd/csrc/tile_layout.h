@@ -33,7 +33,9 @@ namespace pg {
 
 enum DType : int { DT_I8 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
 enum Layout : int { LAYOUT_RR = 0, LAYOUT_RC = 1 };
-enum Variant : int { VAR_REG = 0, VAR_DIRECT = 1 };
+// VAR_REG_KTAIL is VAR_REG for a K that is not a multiple of 16 bytes: its
+// first (ragged) K-tile load reads the partial chunk at K exactly.
+enum Variant : int { VAR_REG = 0, VAR_DIRECT = 1, VAR_REG_KTAIL = 2 };
 enum TileClass : int { TILE_L = 0, TILE_M = 1, TILE_T = 2, TILE_W = 3, TILE_COUNT = 4 };
 
 constexpr int kMaxStages = 4;

@@ -55,6 +55,45 @@ def run_gpu(g, a_cpu, b_cpu, dtype, layout, stages, variant, M, N, K, lda=None, 
     return c.cpu()
 
 
+# Fill for the bytes around a placed operand: NaN for the float types, so a
+# read of any byte past K or outside the rows shows up in C.
+POISON = {"i8": 0x55, "f16": 0x7E00, "bf16": 0x7FC0, "f32": 0x7FC00000}
+
+
+def place(t_cpu, ld, offset, dtype):
+    """A CPU matrix (rows x cols, row-major) copied to the GPU with row
+    stride `ld` elements, starting `offset` elements into a buffer that ends
+    exactly at its last element; every other element holds POISON.
+    Returns (buffer, device pointer of element (0, 0))."""
+    rows, cols = t_cpu.shape
+    n = offset + (rows - 1) * ld + cols if rows > 0 else offset
+    itype = {1: torch.int8, 2: torch.int16, 4: torch.int32}[t_cpu.element_size()]
+    pat = POISON[dtype]
+    bits = 8 * t_cpu.element_size()
+    if pat >= 1 << (bits - 1):
+        pat -= 1 << bits
+    flat = torch.full((max(n, 1),), pat, dtype=itype)
+    raw = t_cpu.contiguous().view(itype)
+    for r in range(rows):
+        flat[offset + r * ld: offset + r * ld + cols] = raw[r]
+    buf = flat.cuda()
+    return buf, buf.data_ptr() + offset * t_cpu.element_size()
+
+
+def run_gpu_placed(g, a_cpu, b_cpu, dtype, layout, stages, variant, M, N, K, lda, ldb, offset,
+                   check=True):
+    """run_gpu with A and B placed by `place` (row strides lda / ldb, both
+    `offset` elements into their buffers).  Returns (status, padded C)."""
+    a_buf, a_ptr = place(a_cpu, lda, offset, dtype)
+    b_buf, b_ptr = place(b_cpu, ldb, offset, dtype)
+    c = alloc_c(M, N, N, dtype)
+    rc = binding.gemm_run(g.h, M, N, K, dtype, layout, stages, variant, a_ptr, lda, b_ptr, ldb, c, N,
+                          check=check)
+    torch.cuda.synchronize()
+    del a_buf, b_buf
+    return rc, c.cpu()
+
+
 def oracle_full(a_cpu, b_cpu, dtype, layout):
     return oracle.gemm(inputs.to_oracle(a_cpu, dtype), inputs.to_oracle(b_cpu, dtype), dtype, layout)
 

@@ -53,10 +53,31 @@ def test_alignment():
     assert q(dtype="i8", K=4104)[0] == A          # i8: K % 16
     assert q(dtype="f32", K=4098)[0] == A
     assert q(lda=4100)[0] == A                    # lda*2 B
+    assert q(ldb=4100)[0] == A                    # RC: ldb*2 B
     assert q(ldc=4098)[0] == A                    # ldc % 4
-    assert q(A=8)[0] == A                         # misaligned pointer
+    assert q(A=8)[0] == A                         # pointer not 16-byte aligned
     assert q(layout="RR", N=4100)[0] == A         # RR: N % 8
     assert q(K=8200)[0] == binding.GEMM_OK        # 8200 * 2 B = 1025 * 16 B
+
+
+def test_register_staged_takes_unaligned_rows():
+    """The register-staged variant takes any K and leading dimension and
+    16-byte-unaligned operand pointers; C's rules and RR's N rule stay."""
+    A, OK = binding.GEMM_ERR_ALIGNMENT, binding.GEMM_OK
+    for stages in (1, 2, 3, 4):
+        assert q(K=4100, variant="reg", stages=stages)[0] == OK
+        assert q(dtype="i8", K=4097, lda=4099, variant="reg", stages=stages)[0] == OK
+        assert q(dtype="f32", K=4098, variant="reg", stages=stages)[0] == OK
+        assert q(layout="RR", K=1001, ldb=4104, variant="reg", stages=stages)[0] == OK
+    assert q(lda=4100, ldb=4098, variant="reg")[0] == OK
+    assert q(A=8, B=24, variant="reg")[0] == OK
+    assert q(dtype="i8", A=9, B=3, variant="reg")[0] == OK
+    assert q(A=9, variant="reg")[0] == A          # bf16: pointer not element-aligned
+    assert q(dtype="f32", B=6, variant="reg")[0] == A
+    assert q(ldc=4098, variant="reg")[0] == A     # C keeps its 16-byte rows
+    assert q(layout="RR", N=4100, variant="reg")[0] == A
+    rc, info = q(K=1001, variant="reg")
+    assert rc == OK and info["k_tiles"] == -(-1001 // info["block_k"]) and info["k_tail"] == 1001 % info["block_k"]
 
 
 def test_unsupported():
