@@ -119,6 +119,9 @@ typedef struct {
     int32_t c_tiles;         /* C tiles; above grid when each workgroup of a
                                 256x256 tile computes several in turn (then
                                 grid = one workgroup per CU) */
+    int32_t splits;          /* K splits per C tile (1: none); see gemm_run_splitk */
+    int32_t reserved;        /* 0 */
+    int64_t workspace_bytes; /* workspace gemm_run_splitk needs (0 when splits = 1) */
 } gemm_config_info_t;
 
 /* Bind a handle to HIP device `device`.  Allocates host memory for the
@@ -133,6 +136,42 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
              int dtype, int layout, int stages, int variant,
              const void *A, int64_t lda, const void *B, int64_t ldb,
              void *C, int64_t ldc, void *stream);
+
+/* C = A * B with K split over `splits` workgroups per C tile, for shapes with
+ * fewer C tiles than compute units (a partial wave: skinny or small M x N
+ * with a long K).  The split count is the analogue, across workgroups, of
+ * what the pages do within one: more independent loads in flight per unit of
+ * C; "CUDA Kernel Study: Pipelining" (Detailed Analysis) and "Part 4 --
+ * Pipelining and Occupancy" (gpucourse.com) tie the gain of pipelining to
+ * the occupancy it leaves.
+ *   splits >= 1 asks for that many (1 = gemm_run); 0 lets the library take
+ *   the smallest that gives every CU a workgroup.  The count used is clamped
+ *   to [1, min(64, K / largest K-tile of the tile class)] and reported by
+ *   gemm_query_splitk.  Each split takes whole units of the class's largest
+ *   K-tile (the ragged rest goes to the last split), so for a given split
+ *   count every (stages, variant) pair still returns bit-identical C.
+ *   Each split writes its fp32 (int32 for GEMM_I8) accumulators to the
+ *   workspace and counts itself in an arrival counter; the split that
+ *   arrives last adds the partial tiles in split order 0, 1, ..., rounds
+ *   once and stores C.  No workgroup waits for another, and the result does
+ *   not depend on which one arrives last.  int8 stays exact.
+ * Workspace: caller-owned device memory of at least
+ *   info.workspace_bytes = 65536 + c_tiles * splits * block_m * block_n * 4
+ *   bytes, 256-byte aligned, overlapping none of A, B, C.  Its first 65536
+ *   bytes hold the arrival counters and must be zero before its first use;
+ *   every call that completes leaves them zero again, so one workspace
+ *   serves any later call, of any shape, on the same stream.  Calls that
+ *   share a workspace must not run concurrently (two streams race).
+ *   NULL / 0 is accepted when the split count used is 1.
+ * Errors: as gemm_run; also GEMM_ERR_INVALID_ARG for splits < 0, a NULL or
+ * too small workspace when splits > 1 are used, GEMM_ERR_ALIGNMENT for a
+ * workspace not 256-byte aligned, GEMM_ERR_UNSUPPORTED for splits > 1 with
+ * more than 16384 C tiles. */
+int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                    int dtype, int layout, int stages, int variant, int splits,
+                    const void *A, int64_t lda, const void *B, int64_t ldb,
+                    void *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                    void *stream);
 
 /* Release a handle.  NULL is a no-op.  Does not synchronise any stream. */
 int gemm_destroy(gemm_handle_t h);
@@ -149,6 +188,13 @@ int gemm_set_tile(gemm_handle_t h, int tile);
 int gemm_query(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
                int variant, int tile, const void *A, int64_t lda, const void *B,
                int64_t ldb, const void *C, int64_t ldc, gemm_config_info_t *info);
+
+/* gemm_query for gemm_run_splitk: the same, with the split count (and the
+ * workspace size) that call would use. */
+int gemm_query_splitk(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+                      int variant, int tile, int splits, const void *A, int64_t lda,
+                      const void *B, int64_t ldb, const void *C, int64_t ldc,
+                      gemm_config_info_t *info);
 
 /* Static text for a status code (never NULL). */
 const char *gemm_status_string(int status);

@@ -25,7 +25,7 @@ TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_T
 
 # C functions exported by the library (the names include/pipegemm.h declares)
 EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",
-           "gemm_status_string", "gemm_last_hip_error")
+           "gemm_run_splitk", "gemm_query_splitk", "gemm_status_string", "gemm_last_hip_error")
 
 
 class GemmError(RuntimeError):
@@ -42,7 +42,8 @@ class ConfigInfo(ctypes.Structure):
         "tile", "block_m", "block_n", "block_k", "waves_m", "waves_n", "threads", "lds_slots",
         "reg_sets", "tiles_in_flight", "lds_bytes", "loads_per_tile")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
-        ("c_tiles", ctypes.c_int32)]
+        ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -69,6 +70,12 @@ def _lib():
         lib.gemm_query.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
                                    ctypes.POINTER(ConfigInfo)]
         lib.gemm_query.restype = ci
+        lib.gemm_run_splitk.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
+                                        vp, i64, vp]
+        lib.gemm_run_splitk.restype = ci
+        lib.gemm_query_splitk.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
+                                          ctypes.POINTER(ConfigInfo)]
+        lib.gemm_query_splitk.restype = ci
         lib.gemm_status_string.argtypes = [ci]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_last_hip_error.argtypes = []
@@ -116,32 +123,47 @@ def gemm_set_tile(h, tile):
         raise GemmError(rc, "gemm_set_tile")
 
 
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
 def gemm_run(h, M, N, K, dtype, layout, stages, variant, A, lda, B, ldb, C, ldc, stream=None,
              check=True):
     """Enqueue C = A * B; returns the status (raises on error when check)."""
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
     rc = _lib().gemm_run(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
-                         _enum(variant, VARIANTS), _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, stream)
+                         _enum(variant, VARIANTS), _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                         _stream(stream))
     if check and rc != GEMM_OK:
         raise GemmError(rc, "gemm_run")
     return rc
 
 
+def gemm_run_splitk(h, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb, C, ldc,
+                    workspace, workspace_bytes, stream=None, check=True):
+    """Enqueue C = A * B with K split over `splits` workgroups per C tile."""
+    rc = _lib().gemm_run_splitk(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
+                                _enum(variant, VARIANTS), int(splits), _ptr(A), lda, _ptr(B), ldb,
+                                _ptr(C), ldc, _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_run_splitk")
+    return rc
+
+
 def gemm_query(M, N, K, dtype, layout, stages, variant, tile="auto", A=0, lda=None, B=0,
-               ldb=None, C=0, ldc=None, check=True):
-    """The configuration gemm_run would use (no HIP call).  Returns (status, dict)."""
+               ldb=None, C=0, ldc=None, check=True, splits=1):
+    """The configuration gemm_run (gemm_run_splitk with `splits`) would use
+    (no HIP call).  Returns (status, dict)."""
     layout_v = _enum(layout, LAYOUTS)
     lda = K if lda is None else lda
     ldb = (N if layout_v == GEMM_LAYOUT_RR else K) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     info = ConfigInfo()
-    rc = _lib().gemm_query(M, N, K, _enum(dtype, DTYPES), layout_v, int(stages),
-                           _enum(variant, VARIANTS), _enum(tile, TILES), A, lda, B, ldb, C, ldc,
-                           ctypes.byref(info))
+    rc = _lib().gemm_query_splitk(M, N, K, _enum(dtype, DTYPES), layout_v, int(stages),
+                                  _enum(variant, VARIANTS), _enum(tile, TILES), int(splits), A, lda, B,
+                                  ldb, C, ldc, ctypes.byref(info))
     if check and rc != GEMM_OK:
         raise GemmError(rc, "gemm_query")
     return rc, info.as_dict()
@@ -154,6 +176,16 @@ class Gemm:
 
     def __init__(self, device=0):
         self.h = gemm_create(device)
+        self.device = device
+        self.tile = "auto"
+        self._ws = None   # split-K workspace: zeroed once, left zeroed by every call
+
+    def workspace(self, nbytes):
+        """A device buffer of at least nbytes for gemm_run_splitk (grown, zeroed, on demand)."""
+        import torch
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device="cuda:%d" % self.device)
+        return self._ws
 
     def close(self):
         if self.h is not None:
@@ -168,12 +200,25 @@ class Gemm:
 
     def set_tile(self, tile):
         gemm_set_tile(self.h, tile)
+        self.tile = tile
 
-    def run(self, a, b, c, dtype, layout, stages, variant, stream=None):
+    def run(self, a, b, c, dtype, layout, stages, variant, stream=None, splits=1):
         M, K = a.shape
         N = b.shape[1] if _enum(layout, LAYOUTS) == GEMM_LAYOUT_RR else b.shape[0]
         for t in (a, b, c):
             if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
                 raise ValueError("operands must be 2-D with unit stride along the last axis")
-        return gemm_run(self.h, M, N, K, dtype, layout, stages, variant,
-                        a, a.stride(0), b, b.stride(0), c, c.stride(0), stream)
+        if splits == 1:
+            return gemm_run(self.h, M, N, K, dtype, layout, stages, variant,
+                            a, a.stride(0), b, b.stride(0), c, c.stride(0), stream)
+        return self.run_splitk(M, N, K, dtype, layout, stages, variant, splits, a, a.stride(0), b,
+                               b.stride(0), c, c.stride(0), stream)
+
+    def run_splitk(self, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb, C, ldc,
+                   stream=None, check=True):
+        """gemm_run_splitk with this handle's tile and workspace."""
+        _, info = gemm_query(M, N, K, dtype, layout, stages, variant, tile=self.tile, lda=lda, ldb=ldb,
+                             ldc=ldc, splits=splits, check=False)
+        ws = self.workspace(info["workspace_bytes"]) if info["workspace_bytes"] > 0 else None
+        return gemm_run_splitk(self.h, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb,
+                               C, ldc, ws, ws.numel() if ws is not None else 0, stream, check)

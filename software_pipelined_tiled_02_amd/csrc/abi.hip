@@ -33,6 +33,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr int64_t kMaxSplits = 64;
+
+// Split-K workspace: the fixed counter area, then every split's BM x BN
+// tile of 4-byte accumulator words.
+int64_t splitk_workspace(int64_t tiles, int64_t splits, const pg::TileShape& ts) {
+    return pg::kSplitkCounterBytes + tiles * splits * ts.bm * ts.bn * 4;
+}
+
 bool instance_exists(int layout, int tile) {
     // both layouts are built at every tile class
     return (layout == pg::LAYOUT_RC || layout == pg::LAYOUT_RR) && tile >= 0 && tile < pg::TILE_COUNT;
@@ -40,7 +48,7 @@ bool instance_exists(int layout, int tile) {
 
 // Every check of the ABI, then the configuration.  No HIP call.
 int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
-              int tile, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+              int tile, int splits, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
               int64_t ldc, int num_cus, bool query, Plan* plan) {
     if (dtype < GEMM_I8 || dtype > GEMM_F32) return GEMM_ERR_INVALID_ARG;
     if (layout != GEMM_LAYOUT_RR && layout != GEMM_LAYOUT_RC) return GEMM_ERR_INVALID_ARG;
@@ -48,6 +56,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (stages < 1 || stages > pg::kMaxStages) return GEMM_ERR_INVALID_ARG;
     if (tile < GEMM_TILE_AUTO || tile >= pg::TILE_COUNT) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
+    if (splits < 0) return GEMM_ERR_INVALID_ARG;
 
     const bool has_c = M > 0 && N > 0;
     const bool reads_a = M > 0 && K > 0 && N > 0;
@@ -121,7 +130,20 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     // one workgroup per CU loops over the tiles, so that one tile's C stores
     // overlap the next tile's first loads.
     in.c_tiles = (int32_t)(tm * tn);
-    in.grid = ((tc == pg::TILE_L || tc == pg::TILE_W) && tm * tn > num_cus && num_cus % 8 == 0) ? num_cus : tm * tn;
+    // Split K: whole units of the class's largest K-tile per split, at most
+    // kMaxSplits.  0 asks for the split that gives every CU a workgroup.
+    const int64_t units = K / pg::block_k(dtype, tc, 1);
+    int64_t P = splits;
+    if (P == 0) P = (tm * tn > 0 && tm * tn < num_cus) ? ceil_div(num_cus, tm * tn) : 1;
+    if (P > units) P = units;
+    if (P > kMaxSplits) P = kMaxSplits;
+    if (P < 1) P = 1;
+    if (P > 1 && tm * tn > pg::kSplitkCounters) return GEMM_ERR_UNSUPPORTED;
+    in.splits = (int32_t)P;
+    in.workspace_bytes = P > 1 ? splitk_workspace(tm * tn, P, ts) : 0;
+    const int64_t work = tm * tn * P;
+    if (work > INT_MAX) return GEMM_ERR_UNSUPPORTED;
+    in.grid = ((tc == pg::TILE_L || tc == pg::TILE_W) && work > num_cus && num_cus % 8 == 0) ? num_cus : work;
     in.k_tiles = ceil_div(K, bk);
     in.k_tail = (int32_t)(K % bk);
     plan->tile = tc;
@@ -194,25 +216,35 @@ int gemm_set_tile(gemm_handle_t h, int tile) {
     return GEMM_OK;
 }
 
-int gemm_query(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
-               int tile, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
-               int64_t ldc, gemm_config_info_t* info) {
+int gemm_query_splitk(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
+                      int tile, int splits, const void* A, int64_t lda, const void* B, int64_t ldb,
+                      const void* C, int64_t ldc, gemm_config_info_t* info) {
     if (info == nullptr) return GEMM_ERR_INVALID_ARG;
     Plan plan;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, A, lda, B, ldb, C, ldc,
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, splits, A, lda, B, ldb, C, ldc,
                        kDefaultCus, true, &plan);
     if (rc == GEMM_OK) *info = plan.info;
     return rc;
 }
 
-int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
-             int variant, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-             int64_t ldc, void* stream) {
-    if (h == nullptr) return GEMM_ERR_INVALID_ARG;
+int gemm_query(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
+               int tile, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
+               int64_t ldc, gemm_config_info_t* info) {
+    return gemm_query_splitk(M, N, K, dtype, layout, stages, variant, tile, 1, A, lda, B, ldb, C, ldc, info);
+}
+
+int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+                    int variant, int splits, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                    int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (h == nullptr || workspace_bytes < 0) return GEMM_ERR_INVALID_ARG;
     Plan plan;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, A, lda, B, ldb, C,
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, A, lda, B, ldb, C,
                        ldc, h->num_cus, false, &plan);
     if (rc != GEMM_OK) return rc;
+    if (plan.info.splits > 1) {
+        if (workspace == nullptr || workspace_bytes < plan.info.workspace_bytes) return GEMM_ERR_INVALID_ARG;
+        if (((uintptr_t)workspace & 255u) != 0) return GEMM_ERR_ALIGNMENT;
+    }
     if (plan.info.grid == 0) return GEMM_OK;
 
     const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
@@ -230,7 +262,8 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int la
     args.K = (int32_t)K;
     args.tiles_m = (int32_t)plan.tiles_m;
     args.tiles_n = (int32_t)plan.tiles_n;
-    args.pad = 0;
+    args.splits = plan.info.splits;
+    args.ws = plan.info.splits > 1 ? workspace : nullptr;
 
     int cur = -1;
     hipError_t e = hipGetDevice(&cur);
@@ -243,6 +276,13 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int la
     if (cur != h->device) hipSetDevice(cur);
     if (e != hipSuccess) return hip_fail(e);
     return GEMM_OK;
+}
+
+int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+             int variant, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+             int64_t ldc, void* stream) {
+    return gemm_run_splitk(h, M, N, K, dtype, layout, stages, variant, 1, A, lda, B, ldb, C, ldc, nullptr, 0,
+                           stream);
 }
 
 const char* gemm_status_string(int status) {

@@ -154,9 +154,11 @@ struct Gemm {
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
         uint32_t rrb[RR ? FN : 1];     // layout RR: per-lane B fragment read offset (step 0)
         uint32_t kb_step;              // byte advance of the B offset per K-tile
-        int K, nt;
+        int K, nt;                     // K; K-tiles this workgroup multiplies
         int head;                      // K-tiles of the ragged head (0, 1 or 2)
         int nbody, rot;                // the other K-tiles; the one they start at
+        int tbase, tail0;              // physical K-tile of body tile 0; of head tile 0
+        uint32_t klast;                // K index the last physical K-tile starts at
         int tid, wave, wm, wn;
     };
 
@@ -170,7 +172,7 @@ struct Gemm {
     // with BK = BKMAX / 2 add the same k-slices in the same order, and every
     // (stages, variant) pair gives bit-identical C.
     __device__ static __forceinline__ int phys_tile(const State& s, int t) {
-        return k_phys_tile(t, s.head, s.nbody, s.rot);
+        return t < s.head ? s.tail0 + t : s.tbase + k_phys_tile(t, s.head, s.nbody, s.rot);
     }
     // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
     // tile, an offset that takes every lane out of the buffer's range.
@@ -188,12 +190,12 @@ struct Gemm {
     // starting at or past K move out of range.
     template <bool FIRST>
     __device__ static __forceinline__ uint32_t voff_a(const State& s, int j) {
-        if (FIRST && s.kca[j] + (uint32_t)(s.nt - 1) * BK >= (uint32_t)s.K) return kOob;
+        if (FIRST && s.kca[j] + s.klast >= (uint32_t)s.K) return kOob;
         return s.offa[j];
     }
     template <bool FIRST>
     __device__ static __forceinline__ uint32_t voff_b(const State& s, int j) {
-        if (FIRST && s.kcb[j] + (uint32_t)(s.nt - 1) * BK >= (uint32_t)s.K) return kOob;
+        if (FIRST && s.kcb[j] + s.klast >= (uint32_t)s.K) return kOob;
         return s.offb[j];
     }
 
@@ -251,7 +253,7 @@ struct Gemm {
     // the matrix; the bytes after vb stay zero.
     __device__ static __forceinline__ i32x4 load_k_tail(const State& s, __amdgpu_buffer_rsrc_t rs, uint32_t off,
                                                        uint32_t kc, uint32_t soff) {
-        int rem = s.K - (int)(kc + (uint32_t)(s.nt - 1) * BK);
+        int rem = s.K - (int)(kc + s.klast);
         // `rem` is the same for every tile; kept opaque, so the compiler forms
         // the offsets below here instead of hoisting them all out of the tile
         // loop into scalar registers (which then spill).
@@ -479,15 +481,97 @@ struct Gemm {
     // (one tile when the grid covers C; several when the host launches one
     // workgroup per CU, so that a tile's C stores overlap the next tile's
     // prologue loads).
+    // Split K: each split writes its accumulators to the workspace as a
+    // BM x BN tile of 4-byte words and counts itself in the tile's arrival
+    // counter.  The split that arrives last adds the partial tiles in split
+    // order 0, 1, ..., rounds once and stores C; the others are done.
+    // Nothing waits for another workgroup, and the sum's order does not
+    // depend on which split is last.  The last one puts the counter back to
+    // 0, so the counters are zero again after every call.
+    //   workspace: kSplitkCounters uint32 counters, then
+    //   [ntiles][splits][BM][BN] accumulator words.
+    __device__ static __forceinline__ void splitk(const GemmArgs& args, uint8_t PG_LDS* smem, const State& s,
+                                                  const acc_t (&acc)[FM][FN], int p, int m0, int n0) {
+        constexpr int PART = BM * BN * 4;
+        const int tile = (m0 / BM) * args.tiles_n + n0 / BN;   // any one-to-one tile number will do
+        uint32_t* cnt = (uint32_t*)args.ws;
+        uint8_t* tp = (uint8_t*)args.ws + kSplitkCounterBytes + (size_t)tile * args.splits * PART;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(tp, 0, 0x7fffffff, kRsrcWord3);
+        // 1. Lane (t, h) holds row t, columns 8q + 4h .. +3 of each 32x32 block
+        //    (per-lane offset in the vector operand, the block's in the scalar one).
+        {
+            const int lane = s.tid & 63, t = lane & 31, h = lane >> 5;
+            const uint32_t vo = (uint32_t)(((s.wm * WTM + t) * BN + s.wn * WTN + 4 * h) * 4);
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)p * PART);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        __builtin_amdgcn_raw_buffer_store_b128(out4_32(acc[fm][fn], q), rw, vo,
+                                                               so + (uint32_t)((fm * 32 * BN + fn * 32 + 8 * q) * 4), 0);
+        }
+        __threadfence();                   // this workgroup's partial is visible device-wide ...
+        block_sync();
+        if (s.tid == 0)                    // ... before it is counted
+            *(volatile uint32_t PG_LDS*)smem = atomicAdd(&cnt[tile], 1u) == (uint32_t)(args.splits - 1);
+        block_sync();
+        if (*(volatile uint32_t PG_LDS*)smem == 0) return;
+        __threadfence();                   // every other split's partial is visible here
+        // 2. Four consecutive columns per lane and step: a wave covers 256
+        //    contiguous words of the tile.
+        for (int it = 0; it < BM * BN / (4 * T); ++it) {
+            const int idx = (it * T + s.tid) * 4;
+            const int m = idx / BN, n = idx % BN;
+            i32x4 sum = {0, 0, 0, 0};
+            for (int q = 0; q < args.splits; ++q) {
+                const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)idx * 4,
+                                                                      __builtin_amdgcn_readfirstlane((uint32_t)q * PART), 0);
+                if constexpr (DT == DT_I8) {
+                    sum += v;
+                } else {
+                    typedef float f32x4 __attribute__((ext_vector_type(4)));
+                    sum = __builtin_bit_cast(i32x4, __builtin_bit_cast(f32x4, sum) + __builtin_bit_cast(f32x4, v));
+                }
+            }
+            if (m0 + m >= args.M) continue;
+            uint8_t* dst = (uint8_t*)args.C + ((int64_t)(m0 + m) * args.ldc + n0 + n) * OSZ;
+            if constexpr (OSZ == 4) {
+                if (n0 + n + 4 <= args.N)
+                    __builtin_nontemporal_store(sum, (i32x4*)dst);
+                else
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + n + e < args.N) *(int*)(dst + 4 * e) = sum[e];
+            } else {
+                typedef float f32x4 __attribute__((ext_vector_type(4)));
+                const f32x4 f = __builtin_bit_cast(f32x4, sum);
+                const i32x2 v = cvt4_16(f[0], f[1], f[2], f[3]);
+                if (n0 + n + 4 <= args.N)
+                    __builtin_nontemporal_store(v, (i32x2*)dst);
+                else
+                    for (int e = 0; e < 4; ++e)
+                        if (n0 + n + e < args.N)
+                            *(uint16_t*)(dst + 2 * e) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        if (s.tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // With K split in `splits` parts, work item j is split j / ntiles of
+    // tile j % ntiles (consecutive workgroups share a K range).
     __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
         const int ntiles = args.tiles_m * args.tiles_n;
-        for (int j = blockIdx.x; j < ntiles; j += gridDim.x) {
+        const int nwork = ntiles * args.splits;
+        for (int j = blockIdx.x; j < nwork; j += gridDim.x) {
             if (j != (int)blockIdx.x) block_sync();   // every wave is done with the last strips
-            run_tile(args, smem, j, ntiles);
+            const int p = j / ntiles;
+            run_tile(args, smem, j - p * ntiles, ntiles, p);
         }
     }
 
-    __device__ static __forceinline__ void run_tile(const GemmArgs args, uint8_t PG_LDS* smem, int j, int ntiles) {
+    __device__ static __forceinline__ void run_tile(const GemmArgs args, uint8_t PG_LDS* smem, int j, int ntiles,
+                                                    int p) {
         State s;
         s.tid = threadIdx.x;
         s.wave = __builtin_amdgcn_readfirstlane(s.tid >> 6);
@@ -513,12 +597,21 @@ struct Gemm {
         const int m0 = tm * BM, n0 = tn * BN;
 
         s.K = args.K;
-        s.nt = (args.K + BK - 1) / BK;
         {
+            // K splits are whole BKMAX-wide units, so that every stage count
+            // adds the same k-slices in the same order; the ragged head goes
+            // with the last split.
             constexpr int BKMAX = block_k(DT, TC, 1);
             static_assert(BKMAX % BK == 0 && (BKMAX == BK || STAGES >= 3), "head tiles are all in the prologue");
-            s.head = k_head_tiles(args.K, BK, BKMAX);
-            s.nbody = s.nt - s.head;
+            const int head = k_head_tiles(args.K, BK, BKMAX);
+            const int units = args.K / BKMAX, per = BKMAX / BK;
+            const int u0 = p * units / args.splits, u1 = (p + 1) * units / args.splits;
+            s.head = (p == args.splits - 1) ? head : 0;
+            s.nbody = (u1 - u0) * per;
+            s.nt = s.nbody + s.head;
+            s.tbase = u0 * per;
+            s.tail0 = units * per;
+            s.klast = (uint32_t)(units * per + head - 1) * BK;
         }
         // Start the K loop of the tiles on XCD x at full tile 9x (mod the
         // count): with every XCD reading the same K columns at once, the
@@ -689,6 +782,11 @@ struct Gemm {
             }
         }
 
+        if (args.splits > 1) {
+            splitk(args, smem, s, acc, p, m0, n0);
+            return;
+        }
+
         // Epilogue.  Lane (t, h) holds C[m][n .. n+3] of each 32x32 block
         // (m = row t of the block, n = 8q + 4h), so a direct store would
         // scatter 8-16 bytes over 32 rows per instruction.  Instead each
@@ -773,8 +871,12 @@ struct Gemm {
         return i32x4{ai[4 * q], ai[4 * q + 1], ai[4 * q + 2], ai[4 * q + 3]};
     }
     __device__ static __forceinline__ i32x2 out4_16(const acc_t& a, int q) {
+        return cvt4_16(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+    }
+    // Four fp32 values rounded to the 16-bit output type (nearest even), packed.
+    __device__ static __forceinline__ i32x2 cvt4_16(float a0, float a1, float a2, float a3) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 lo = {a[4 * q], a[4 * q + 1]}, hi = {a[4 * q + 2], a[4 * q + 3]};
+        const f32x2 lo = {a0, a1}, hi = {a2, a3};
         if constexpr (DT == DT_BF16) {
             typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
             return i32x2{__builtin_bit_cast(int, __builtin_convertvector(lo, bf16x2)),
@@ -798,7 +900,7 @@ pipegemm_kernel(GemmArgs args) {
     a.A = args.A; a.B = args.B; a.C = args.C;
     a.lda = args.lda; a.ldb = args.ldb; a.ldc = args.ldc;
     a.M = args.M; a.N = args.N; a.K = args.K;
-    a.tiles_m = args.tiles_m; a.tiles_n = args.tiles_n; a.pad = 0;
+    a.tiles_m = args.tiles_m; a.tiles_n = args.tiles_n; a.splits = args.splits; a.ws = args.ws;
     G::run(a, (uint8_t PG_LDS*)smem_raw);
 }
 

@@ -7,6 +7,12 @@
 
 namespace pg {
 
+// Split-K workspace: a fixed area of uint32 arrival counters, one per C tile
+// (so a workspace reused for another shape finds its counters where the
+// last call left them: zero), then the partial tiles.
+constexpr int kSplitkCounters = 16384;
+constexpr int64_t kSplitkCounterBytes = (int64_t)kSplitkCounters * 4;
+
 struct GemmArgs {
     const void* A;      // row-major M x K
     const void* B;      // row-major K x N (RR) or column-major K x N (RC)
@@ -14,7 +20,8 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;  // in elements
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;
-    int32_t pad;
+    int32_t splits;     // K splits per C tile (1: none)
+    void* ws;           // splits > 1: per-tile arrival counters, then the partial tiles
 };
 
 struct KernelEntry {

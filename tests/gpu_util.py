@@ -94,6 +94,19 @@ def run_gpu_placed(g, a_cpu, b_cpu, dtype, layout, stages, variant, M, N, K, lda
     return rc, c.cpu()
 
 
+def run_gpu_splitk(g, a_cpu, b_cpu, dtype, layout, stages, variant, M, N, K, splits):
+    """run_gpu through gemm_run_splitk with the handle's workspace; returns
+    (padded C on the CPU, the configuration used)."""
+    ldb = N if layout == "RR" else K
+    ldc = (N + 3) // 4 * 4                    # C rows: whole 16-byte groups of 4-byte words
+    a, b = a_cpu.cuda(), b_cpu.cuda()
+    c = alloc_c(M, N, ldc, dtype)
+    _, info = binding.gemm_query(M, N, K, dtype, layout, stages, variant, tile=g.tile, ldc=ldc, splits=splits)
+    g.run_splitk(M, N, K, dtype, layout, stages, variant, splits, a, K, b, ldb, c, ldc)
+    torch.cuda.synchronize()
+    return c.cpu(), info
+
+
 def oracle_full(a_cpu, b_cpu, dtype, layout):
     return oracle.gemm(inputs.to_oracle(a_cpu, dtype), inputs.to_oracle(b_cpu, dtype), dtype, layout)
 

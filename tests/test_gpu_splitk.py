@@ -1,0 +1,150 @@
+"""GPU parity of the split-K entry point (gemm_run_splitk) against the oracle.
+
+Shapes with fewer C tiles than compute units and a long K, every tile class,
+layout, dtype, stage count and variant; for a fixed split count all
+(stages, variant) pairs must also agree bit for bit, since each split adds
+whole units of the class's largest K-tile in one k order and the partial
+tiles are added in split order.  The workspace's arrival counters must come
+back to zero after every call, so a second call, and a call of another
+shape, on the same workspace give the same results.
+"""
+import pytest
+import torch
+
+from software_pipelined_tiled_02_amd import binding, inputs
+from tests.gpu_util import (EPC, alloc_c, check_close, check_sentinel, oracle_full, run_gpu_placed,
+                            run_gpu_splitk)
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("i8", "f16", "bf16", "f32")
+LAYOUT_TILES = [("RC", "256x256"), ("RC", "256x256w8"), ("RC", "128x128"), ("RC", "32x64"),
+                ("RR", "256x256"), ("RR", "256x256w8"), ("RR", "128x128"), ("RR", "32x64")]
+DIST = {"i8": "int", "f16": "normal", "bf16": "uniform", "f32": "uniform"}
+
+
+@pytest.fixture(scope="module")
+def g():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gg = binding.Gemm(0)
+    yield gg
+    gg.close()
+
+
+def _k(dtype):
+    # 6 units of the 128x128 class's K-tile plus a ragged rest of three chunks
+    return 6 * 8 * EPC[dtype] + 3 * EPC[dtype]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout,tile", LAYOUT_TILES)
+def test_splitk_all_stages_variants(g, dtype, layout, tile):
+    # N: a multiple of 16 for layout RR (its rule), not of 4 for RC (masked column tail)
+    M, N, K = 300, (144 if layout == "RR" else 138), _k(dtype)
+    a, b = inputs.make_operands(M, N, K, dtype, layout, DIST[dtype], seed=21)
+    ref = oracle_full(a, b, dtype, layout)
+    g.set_tile(tile)
+    try:
+        for splits in (2, 3, 5):
+            first = None
+            for stages in (1, 2, 3, 4):
+                for variant in ("reg", "direct"):
+                    what = "%s %s %s splits=%d S=%d %s" % (dtype, layout, tile, splits, stages, variant)
+                    print("case:", what, flush=True)
+                    c, info = run_gpu_splitk(g, a, b, dtype, layout, stages, variant, M, N, K, splits)
+                    assert info["splits"] == min(splits, K // (info["block_k"] * (2 if stages >= 3 and
+                                                 tile.startswith("256") else 1))), info
+                    check_sentinel(c, M, N, dtype)
+                    check_close(c[:M, :N], ref, dtype, what)
+                    if first is None:
+                        first = c
+                    else:
+                        assert torch.equal(c.view(torch.uint8), first.view(torch.uint8)), \
+                            what + ": not bit-identical to S=1 reg"
+    finally:
+        g.set_tile("auto")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_splitk_auto_partial_wave(g, dtype):
+    """1024 x 512 with a long K: 32 tiles of 128x128, auto split 8."""
+    M, N, K = 1024, 512, 4096 + 2 * EPC[dtype]
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=4)
+    ref = oracle_full(a, b, dtype, "RC")
+    g.set_tile("128x128")
+    try:
+        c, info = run_gpu_splitk(g, a, b, dtype, "RC", 2, "direct", M, N, K, 0)
+        assert info["splits"] == 8 and info["grid"] == 256, info
+        check_sentinel(c, M, N, dtype)
+        check_close(c[:M, :N], ref, dtype, "%s auto split" % dtype)
+    finally:
+        g.set_tile("auto")
+
+
+def test_splitk_workspace_reuse(g):
+    """Repeated calls and a call of another shape on one workspace: the
+    counters are zero again after each call."""
+    dtype = "bf16"
+    g.set_tile("128x128")
+    try:
+        shapes = [(256, 256, 2048), (640, 384, 3072), (256, 256, 2048)]
+        results = {}
+        for M, N, K in shapes:
+            a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=M + K)
+            ref = oracle_full(a, b, dtype, "RC")
+            for rep in range(2):
+                print("case: reuse", M, N, K, rep, flush=True)
+                c, info = run_gpu_splitk(g, a, b, dtype, "RC", 3, "direct", M, N, K, 4)
+                assert info["splits"] == 4
+                check_close(c[:M, :N], ref, dtype, "reuse %s" % ((M, N, K),))
+                key = (M, N, K)
+                if key in results:
+                    assert torch.equal(c.view(torch.uint8), results[key].view(torch.uint8))
+                results[key] = c
+        counters = g.workspace(65536)[:65536]
+        assert int(counters.count_nonzero()) == 0, "arrival counters not back to zero"
+    finally:
+        g.set_tile("auto")
+
+
+@pytest.mark.parametrize("dtype", ("i8", "bf16"))
+def test_splitk_unaligned_k(g, dtype):
+    """The register-staged variant's ragged-K instances under a split."""
+    M, N, K = 200, 96, 1501
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=8)
+    ref = oracle_full(a, b, dtype, "RC")
+    g.set_tile("128x128")
+    try:
+        first = None
+        for stages in (1, 2, 3, 4):
+            c, info = run_gpu_splitk(g, a, b, dtype, "RC", stages, "reg", M, N, K, 4)
+            assert info["splits"] == 4
+            check_close(c[:M, :N], ref, dtype, "%s K=%d S=%d split 4" % (dtype, K, stages))
+            if first is None:
+                first = c
+            else:
+                assert torch.equal(c.view(torch.uint8), first.view(torch.uint8))
+    finally:
+        g.set_tile("auto")
+
+
+def test_splitk_workspace_errors(g):
+    """A missing, short or misaligned workspace is refused and C is left alone."""
+    M, N, K, dtype = 256, 256, 2048, "bf16"
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=2)
+    a, b = a.cuda(), b.cuda()
+    c = alloc_c(M, N, N, dtype)
+    _, info = binding.gemm_query(M, N, K, dtype, "RC", 2, "direct", splits=4)
+    need = info["workspace_bytes"]
+    assert info["splits"] == 4 and need > 0
+    ws = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+    run = lambda w, nbytes: binding.gemm_run_splitk(g.h, M, N, K, dtype, "RC", 2, "direct", 4, a, K, b, K,
+                                                   c, N, w, nbytes, check=False)
+    assert run(None, 0) == binding.GEMM_ERR_INVALID_ARG
+    assert run(ws, need - 1) == binding.GEMM_ERR_INVALID_ARG
+    assert run(ws.data_ptr() + 16, need) == binding.GEMM_ERR_ALIGNMENT
+    torch.cuda.synchronize()
+    check_sentinel(c.cpu(), 0, N, dtype)
+    assert run(ws, need) == binding.GEMM_OK
+    torch.cuda.synchronize()
+    assert int(ws[:65536].count_nonzero()) == 0

@@ -150,3 +150,50 @@ def test_create_rejects_bad_arguments_without_gpu():
     assert lib.gemm_create(ctypes.byref(h), -1) == binding.GEMM_ERR_INVALID_ARG
     assert lib.gemm_destroy(None) == binding.GEMM_OK
     assert lib.gemm_run(None, 1, 1, 16, 2, 1, 1, 1, 16, 16, 16, 16, 16, 4, None) == binding.GEMM_ERR_INVALID_ARG
+
+
+def test_splitk_plan():
+    """Split count, clamping and workspace size as the header states."""
+    OK = binding.GEMM_OK
+    # a partial wave: 1024 x 1024 at 128x128 is 64 tiles for 256 CUs
+    rc, info = q(M=1024, N=1024, K=8192, tile="128x128", splits=0)
+    assert rc == OK and info["c_tiles"] == 64 and info["splits"] == 4 and info["grid"] == 256
+    assert info["workspace_bytes"] == 65536 + 64 * 4 * 128 * 128 * 4
+    # explicit counts; clamped to K / (the class's largest K-tile) and to 64
+    rc, info = q(M=1024, N=1024, K=8192, tile="128x128", splits=3)
+    assert rc == OK and info["splits"] == 3 and info["grid"] == 192
+    rc, info = q(M=1024, N=1024, K=200, tile="128x128", splits=8)     # bf16 BK 64: 3 whole units
+    assert rc == OK and info["splits"] == 3
+    rc, info = q(M=1024, N=1024, K=56, tile="128x128", splits=8)      # less than one unit: no split
+    assert rc == OK and info["splits"] == 1 and info["workspace_bytes"] == 0
+    rc, info = q(M=64, N=64, K=1 << 20, tile="32x64", splits=100)
+    assert rc == OK and info["splits"] == 64
+    # enough tiles already: auto takes no split; splits = 1 is gemm_run's plan
+    rc, info = q(splits=0)
+    assert rc == OK and info["splits"] == 1 and info["workspace_bytes"] == 0
+    assert q(splits=1)[1] == q()[1]
+    # the 256x256 tiles loop over work items when there are more than CUs
+    rc, info = q(M=2048, N=2048, K=8192, tile="256x256", splits=8)
+    assert rc == OK and info["c_tiles"] == 64 and info["splits"] == 8 and info["grid"] == 256
+    # stages and variants share the split's K units (largest K-tile of the class)
+    for stages in (1, 2, 3, 4):
+        for variant in ("reg", "direct"):
+            rc, info = q(M=512, N=512, K=8192, tile="256x256", stages=stages, variant=variant, splits=0)
+            assert rc == OK and info["splits"] == 64
+
+
+def test_splitk_arguments():
+    E, A, U = binding.GEMM_ERR_INVALID_ARG, binding.GEMM_ERR_ALIGNMENT, binding.GEMM_ERR_UNSUPPORTED
+    assert q(splits=-1)[0] == E
+    # more than 16384 C tiles cannot take a split
+    assert q(M=8192, N=8192 * 4, K=8192, tile="32x64", splits=2)[0] == U
+    assert q(M=8192, N=8192 * 4, K=8192, tile="32x64", splits=1)[0] == binding.GEMM_OK
+
+
+def test_splitk_run_rejects_null_handle():
+    """gemm_run_splitk checks its handle before anything else (the workspace
+    checks need a device and are GPU-tested)."""
+    lib = binding.library()
+    rc = lib.gemm_run_splitk(None, 1024, 1024, 8192, 2, 1, 2, 1, 4, 16, 8192, 16, 8192, 16, 1024,
+                             256, 1 << 30, None)
+    assert rc == binding.GEMM_ERR_INVALID_ARG
