@@ -49,6 +49,11 @@ WORKLOADS = {
                      "fp16 GEMM M=N=K=4096, A and B row-major (B read with transposing LDS reads)"),
     "int8_4096_rr": (4096, 4096, 4096, "i8", "RR", "int", 1.0, "mfma",
                      "int8 IGEMM M=N=K=4096, A and B row-major (B read with transposing LDS reads)"),
+    "bf16_1024x1024x8192": (1024, 1024, 8192, "bf16", "RC", "uniform", 1.0, "mfma",
+                            "bf16 GEMM M=N=1024 K=8192 (few C tiles, long K), fp32 accumulate, bf16 out"),
+    "bf16_1024x8192x8200": (1024, 8192, 8200, "bf16", "RC", "uniform", 1.0, "mfma",
+                            "bf16 GEMM M=1024 N=8192 K=8200 (one GPU's share of M=N=8192 K=8200 "
+                            "split 8 ways along M), fp32 accumulate, bf16 out"),
 }
 DEFAULT_WORKLOAD = "int8_4096"
 
@@ -135,6 +140,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--pairs", default="all", help="comma list like 3:direct,2:reg, or all")
     ap.add_argument("--tile", default="auto", help="tile class: auto, 256x256, 256x256w8, 128x128, 32x64")
+    ap.add_argument("--splits", type=int, default=1,
+                    help="K splits per C tile (gemm_run_splitk); 0 = the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     args = ap.parse_args()
@@ -173,9 +180,22 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
+    if args.splits != 1:
+        # the split-K workspace, allocated (zeroed) once, before anything is timed
+        for s, v in pairs:
+            _, qi = binding.gemm_query(M, N, K, dtype, layout, s, v, tile=args.tile, splits=args.splits)
+            g.workspace(qi["workspace_bytes"])
+    ws = g.workspace(1) if args.splits != 1 else None
+
+    def run_one(aa, bb, cc, s, v):
+        if args.splits == 1:
+            binding.gemm_run(g.h, M, N, K, dtype, layout, s, v, aa, K, bb, ldb, cc, N, sh)
+        else:
+            binding.gemm_run_splitk(g.h, M, N, K, dtype, layout, s, v, args.splits, aa, K, bb, ldb, cc, N,
+                                    ws, ws.numel(), sh)
+
     def launch(i, s, v):
-        aa, bb, cc = sets[i % nrot]
-        binding.gemm_run(g.h, M, N, K, dtype, layout, s, v, aa, K, bb, ldb, cc, N, sh)
+        run_one(*sets[i % nrot], s, v)
 
     ops = flops(M, N, K)
     algo_bytes = set_bytes
@@ -237,7 +257,7 @@ def main():
 
     best = min(results, key=lambda p: results[p]["mean_us"])
     r = results[best]
-    _, info = binding.gemm_query(M, N, K, dtype, layout, best[0], best[1], tile=args.tile)
+    _, info = binding.gemm_query(M, N, K, dtype, layout, best[0], best[1], tile=args.tile, splits=args.splits)
     unit = "TOP/s" if dtype == "i8" else "TFLOP/s"
     if bound == "hbm":
         value, vunit = r["gbs"], "GB/s"
@@ -258,12 +278,12 @@ def main():
         # The same buffers every launch: A fits in the Infinity Cache, so this
         # is a cache-resident figure, reported beside (never as) the value.
         for _ in range(args.warmup):
-            binding.gemm_run(g.h, M, N, K, dtype, layout, best[0], best[1], a, K, b, ldb, sets[0][2], N, sh)
+            run_one(a, b, sets[0][2], best[0], best[1])
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
         for _ in range(args.steps):
-            binding.gemm_run(g.h, M, N, K, dtype, layout, best[0], best[1], a, K, b, ldb, sets[0][2], N, sh)
+            run_one(a, b, sets[0][2], best[0], best[1])
         t1.record(stream)
         torch.cuda.synchronize()
         hot_ms = t0.elapsed_time(t1) / args.steps
@@ -281,7 +301,7 @@ def main():
         "config": {"workload": desc, "M": M, "N": N, "K": K, "layout": layout,
                    "stages": best[0], "variant": best[1],
                    "tile": "%dx%dx%d" % (info["block_m"], info["block_n"], info["block_k"]),
-                   "lds_bytes": info["lds_bytes"], "grid": info["grid"]},
+                   "lds_bytes": info["lds_bytes"], "grid": info["grid"], "splits": info["splits"]},
         "roofline": roof,
         "pairs_bit_identical": identical,
         "sweep": {"S%d_%s" % p: {"us": q["mean_us"], "per_launch_median_us": q["median_us"],

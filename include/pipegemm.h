@@ -145,7 +145,9 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
  * Pipelining and Occupancy" (gpucourse.com) tie the gain of pipelining to
  * the occupancy it leaves.
  *   splits >= 1 asks for that many (1 = gemm_run); 0 lets the library take
- *   the smallest that gives every CU a workgroup.  The count used is clamped
+ *   the smallest that gives every CU a workgroup, but at most 8 and with at
+ *   least two K units per split (the last split reads every partial tile,
+ *   so the final sum grows with the count).  The count used is clamped
  *   to [1, min(64, K / largest K-tile of the tile class)] and reported by
  *   gemm_query_splitk.  Each split takes whole units of the class's largest
  *   K-tile (the ragged rest goes to the last split), so for a given split

@@ -34,6 +34,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxSplits = 64;
+constexpr int64_t kAutoSplits = 8;
 
 // Split-K workspace: the fixed counter area, then every split's BM x BN
 // tile of 4-byte accumulator words.
@@ -131,10 +132,19 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     // overlap the next tile's first loads.
     in.c_tiles = (int32_t)(tm * tn);
     // Split K: whole units of the class's largest K-tile per split, at most
-    // kMaxSplits.  0 asks for the split that gives every CU a workgroup.
+    // kMaxSplits.  0 asks for the split that gives every CU a workgroup, at
+    // most kAutoSplits and at least two units per split: the split that
+    // arrives last reads every partial tile, so the final sum grows with the
+    // split count (measured on 1024 x 1024 x 8192 bf16 with 256 x 256
+    // tiles: 177 us at 8 splits, 320 us at 16, against 45 us for 128 x 128
+    // tiles at 4).
     const int64_t units = K / pg::block_k(dtype, tc, 1);
     int64_t P = splits;
-    if (P == 0) P = (tm * tn > 0 && tm * tn < num_cus) ? ceil_div(num_cus, tm * tn) : 1;
+    if (P == 0) {
+        P = (tm * tn > 0 && tm * tn < num_cus) ? ceil_div(num_cus, tm * tn) : 1;
+        if (P > kAutoSplits) P = kAutoSplits;
+        if (P > units / 2) P = units / 2;
+    }
     if (P > units) P = units;
     if (P > kMaxSplits) P = kMaxSplits;
     if (P < 1) P = 1;

@@ -67,6 +67,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kRsrcWord3 = 0x00020000;
 // A buffer offset no valid element reaches: loads from it return zero.
 constexpr uint32_t kOob = 0x80000000u;
+// Cache-policy operand of a buffer access at device scope (the SC1 bit):
+// coherent across the XCDs' L2 caches.
+constexpr int kScopeDevice = 16;
 
 template <int DT> struct AccT { typedef f32x16 type; };
 template <> struct AccT<DT_I8> { typedef i32x16 type; };
@@ -488,6 +491,12 @@ struct Gemm {
     // Nothing waits for another workgroup, and the sum's order does not
     // depend on which split is last.  The last one puts the counter back to
     // 0, so the counters are zero again after every call.
+    //   Visibility across XCDs (each has its own L2) without an L2-wide
+    // write-back or invalidate: the partials are written and read with
+    // device-scope stores and loads (the scope bits of the buffer
+    // instructions: written through to memory, read from it), every store
+    // has completed before the counter is incremented, and the partials are
+    // read only after the increment that finds all the others.
     //   workspace: kSplitkCounters uint32 counters, then
     //   [ntiles][splits][BM][BN] accumulator words.
     __device__ static __forceinline__ void splitk(const GemmArgs& args, uint8_t PG_LDS* smem, const State& s,
@@ -510,49 +519,42 @@ struct Gemm {
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         __builtin_amdgcn_raw_buffer_store_b128(out4_32(acc[fm][fn], q), rw, vo,
-                                                               so + (uint32_t)((fm * 32 * BN + fn * 32 + 8 * q) * 4), 0);
+                                                               so + (uint32_t)((fm * 32 * BN + fn * 32 + 8 * q) * 4),
+                                                               kScopeDevice);
         }
-        __threadfence();                   // this workgroup's partial is visible device-wide ...
+        wait_vmcnt<0>();                   // this workgroup's partial has reached memory ...
         block_sync();
         if (s.tid == 0)                    // ... before it is counted
-            *(volatile uint32_t PG_LDS*)smem = atomicAdd(&cnt[tile], 1u) == (uint32_t)(args.splits - 1);
+            *(volatile uint32_t PG_LDS*)smem =
+                __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(args.splits - 1);
         block_sync();
         if (*(volatile uint32_t PG_LDS*)smem == 0) return;
-        __threadfence();                   // every other split's partial is visible here
-        // 2. Four consecutive columns per lane and step: a wave covers 256
-        //    contiguous words of the tile.
-        for (int it = 0; it < BM * BN / (4 * T); ++it) {
-            const int idx = (it * T + s.tid) * 4;
-            const int m = idx / BN, n = idx % BN;
-            i32x4 sum = {0, 0, 0, 0};
+        // 2. Four consecutive columns per lane and chunk (a wave covers 256
+        //    contiguous words of the tile), each split's added in split
+        //    order.  (Batching chunks, U > 1, raised the register peak of
+        //    the whole kernel and cost waves per SIMD in some instances.)
+        constexpr int ITER = BM * BN / (4 * T), U = 1;
+        static_assert(ITER % U == 0, "split-K chunks");
+        for (int it0 = 0; it0 < ITER; it0 += U) {
+            i32x4 sum[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) sum[u] = i32x4{0, 0, 0, 0};
             for (int q = 0; q < args.splits; ++q) {
-                const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)idx * 4,
-                                                                      __builtin_amdgcn_readfirstlane((uint32_t)q * PART), 0);
-                if constexpr (DT == DT_I8) {
-                    sum += v;
-                } else {
-                    typedef float f32x4 __attribute__((ext_vector_type(4)));
-                    sum = __builtin_bit_cast(i32x4, __builtin_bit_cast(f32x4, sum) + __builtin_bit_cast(f32x4, v));
-                }
+                i32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rw, (uint32_t)(((it0 + u) * T + s.tid) * 16), __builtin_amdgcn_readfirstlane((uint32_t)q * PART),
+                        kScopeDevice);
+#pragma unroll
+                for (int u = 0; u < U; ++u) sum[u] = add_acc(sum[u], v[u]);
             }
-            if (m0 + m >= args.M) continue;
-            uint8_t* dst = (uint8_t*)args.C + ((int64_t)(m0 + m) * args.ldc + n0 + n) * OSZ;
-            if constexpr (OSZ == 4) {
-                if (n0 + n + 4 <= args.N)
-                    __builtin_nontemporal_store(sum, (i32x4*)dst);
-                else
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + n + e < args.N) *(int*)(dst + 4 * e) = sum[e];
-            } else {
-                typedef float f32x4 __attribute__((ext_vector_type(4)));
-                const f32x4 f = __builtin_bit_cast(f32x4, sum);
-                const i32x2 v = cvt4_16(f[0], f[1], f[2], f[3]);
-                if (n0 + n + 4 <= args.N)
-                    __builtin_nontemporal_store(v, (i32x2*)dst);
-                else
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + n + e < args.N)
-                            *(uint16_t*)(dst + 2 * e) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = ((it0 + u) * T + s.tid) * 4;
+                const int m = idx / BN, n = idx % BN;
+                if (m0 + m < args.M) store_out4(args, m0 + m, n0 + n, sum[u]);
             }
         }
         if (s.tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -872,6 +874,38 @@ struct Gemm {
     }
     __device__ static __forceinline__ i32x2 out4_16(const acc_t& a, int q) {
         return cvt4_16(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+    }
+    // a + b as accumulator words (int32 for int8, fp32 otherwise).
+    __device__ static __forceinline__ i32x4 add_acc(const i32x4 a, const i32x4 b) {
+        if constexpr (DT == DT_I8) {
+            return a + b;
+        } else {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            return __builtin_bit_cast(i32x4, __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b));
+        }
+    }
+    // C[m][n .. n+3] from four accumulator words: converted to the output
+    // type, masked at column N.
+    __device__ static __forceinline__ void store_out4(const GemmArgs& args, int m, int n, const i32x4 w) {
+        uint8_t* dst = (uint8_t*)args.C + ((int64_t)m * args.ldc + n) * OSZ;
+        if constexpr (OSZ == 4) {
+            if (n + 4 <= args.N) {
+                __builtin_nontemporal_store(w, (i32x4*)dst);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < args.N) *(int*)(dst + 4 * e) = w[e];
+            }
+        } else {
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            const f32x4 f = __builtin_bit_cast(f32x4, w);
+            const i32x2 v = cvt4_16(f[0], f[1], f[2], f[3]);
+            if (n + 4 <= args.N) {
+                __builtin_nontemporal_store(v, (i32x2*)dst);
+            } else {
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < args.N) *(uint16_t*)(dst + 2 * e) = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
     }
     // Four fp32 values rounded to the 16-bit output type (nearest even), packed.
     __device__ static __forceinline__ i32x2 cvt4_16(float a0, float a1, float a2, float a3) {

@@ -107,6 +107,24 @@ def test_splitk_workspace_reuse(g):
         g.set_tile("auto")
 
 
+@pytest.mark.parametrize("dtype", ("i8", "f32"))
+def test_splitk_new_inputs_same_workspace(g, dtype):
+    """The same shape on the same workspace with new inputs, call after call:
+    a partial read before it was written (or a stale copy of the last
+    call's) would show as a wrong C."""
+    M, N, K = 512, 320, 4096
+    g.set_tile("128x128")
+    try:
+        for seed in range(6):
+            a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=100 + seed)
+            ref = oracle_full(a, b, dtype, "RC")
+            c, info = run_gpu_splitk(g, a, b, dtype, "RC", 2, "direct", M, N, K, 0)
+            assert info["splits"] > 1
+            check_close(c[:M, :N], ref, dtype, "%s seed %d" % (dtype, seed))
+    finally:
+        g.set_tile("auto")
+
+
 @pytest.mark.parametrize("dtype", ("i8", "bf16"))
 def test_splitk_unaligned_k(g, dtype):
     """The register-staged variant's ragged-K instances under a split."""

@@ -179,7 +179,12 @@ def test_splitk_plan():
     for stages in (1, 2, 3, 4):
         for variant in ("reg", "direct"):
             rc, info = q(M=512, N=512, K=8192, tile="256x256", stages=stages, variant=variant, splits=0)
+            assert rc == OK and info["splits"] == 8          # the automatic choice stops at 8
+            rc, info = q(M=512, N=512, K=8192, tile="256x256", stages=stages, variant=variant, splits=64)
             assert rc == OK and info["splits"] == 64
+    # the automatic choice leaves at least two K units per split
+    rc, info = q(M=256, N=256, K=5 * 64, tile="256x256", splits=0)
+    assert rc == OK and info["splits"] == 2
 
 
 def test_splitk_arguments():
