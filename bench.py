@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the pipelined tiled GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rounds R] [--workload NAME]
+                    [--tile T] [--splits P]
 
 A step is one C = A * B launch (the whole K-loop pipeline: prologue, main
 loop, drain, epilogue) over one synthetic input set.  After half a second
 of untimed launches that lets the GPU clocks settle, every (stages,
-variant) pair of the chosen workload is timed: W untimed warm-up steps,
-then exactly K steps launched back to back between two HIP events recorded
-on the stream the kernel is launched on (synchronised on both sides); the
-mean launch duration is that interval over K.  A second pass of K launches,
-each between its own events, gives the spread (per_launch_* in "sweep").
+variant) pair of the chosen workload is timed, in R rounds over all pairs:
+each time W untimed warm-up steps, then exactly K steps launched back to
+back between two HIP events recorded on the stream the kernel is launched
+on (synchronised on both sides); the launch duration is that interval over
+K, and a pair reports its median round (all rounds are in "rounds_us").  A
+last pass of K launches per pair, each between its own events, gives the
+spread (per_launch_* in "sweep").
 Inputs rotate over enough copies that the footprint exceeds 512 MiB, so
 the 256 MB Infinity Cache cannot hold them.
 The headline is the fastest pair; all pairs are in "sweep".
@@ -137,6 +140,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--rounds", type=int, default=3, help="rounds over all pairs; each pair reports its median")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--pairs", default="all", help="comma list like 3:direct,2:reg, or all")
     ap.add_argument("--tile", default="auto", help="tile class: auto, 256x256, 256x256w8, 128x128, 32x64")
@@ -209,27 +213,43 @@ def main():
             launch(i, *pairs[0])
             i += 1
         torch.cuda.synchronize()
-    results = {}
+    # The sweep runs in `rounds` rounds, each timing every pair once; a pair
+    # is reported by its median round.  (Measured in one sweep, the same
+    # kernel came out 20-30% slower when it happened to be timed third, a
+    # window in which the chip's clock drops; rounds spread every pair over
+    # the run instead of tying it to one moment.)
+    rounds = {p: [] for p in pairs}
     first_c = None          # C of the first pair: every pair must reproduce it bit for bit
     identical = True
+    for rnd in range(args.rounds):
+        for s, v in pairs:
+            for i in range(args.warmup):
+                launch(i, s, v)
+            torch.cuda.synchronize()
+            # The timed region: K launches back to back between two events on
+            # the launch stream, synchronised on both sides.
+            t_start = torch.cuda.Event(enable_timing=True)
+            t_end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t_start.record(stream)
+            for i in range(args.steps):
+                launch(i, s, v)
+            t_end.record(stream)
+            torch.cuda.synchronize()
+            rounds[(s, v)].append(t_start.elapsed_time(t_end) / args.steps)   # ms per launch
+            if rnd == 0:
+                c0 = sets[0][2].view(torch.uint8)
+                if first_c is None:
+                    first_c = c0.clone()
+                elif not torch.equal(c0, first_c):
+                    identical = False
+                    print("# S=%d %s: C differs bitwise from the first pair" % (s, v), file=sys.stderr, flush=True)
+    results = {}
     for s, v in pairs:
-        for i in range(args.warmup):
-            launch(i, s, v)
-        torch.cuda.synchronize()
-        # The timed region: K launches back to back between two events on
-        # the launch stream, synchronised on both sides.
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        for i in range(args.steps):
-            launch(i, s, v)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total = t_start.elapsed_time(t_end)                       # ms
-        mean = total / args.steps
-        # Spread (informational): the same K launches, each between its own
-        # pair of events (which adds the event records' gaps to each).
+        rs = rounds[(s, v)]
+        mean = sorted(rs)[len(rs) // 2]                            # median round, ms per launch
+        # Spread (informational): K launches, each between its own pair of
+        # events (which adds the event records' gaps to each).
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         for i in range(args.steps):
@@ -241,19 +261,14 @@ def main():
         results[(s, v)] = {
             "mean_us": round(mean * 1e3, 2), "median_us": round(per[len(per) // 2] * 1e3, 2),
             "min_us": round(per[0] * 1e3, 2), "max_us": round(per[-1] * 1e3, 2),
+            "rounds_us": [round(x * 1e3, 2) for x in rs],
             "ms_per_step": mean,
             "tops": ops / (mean * 1e-3) / 1e12, "gbs": algo_bytes / (mean * 1e-3) / 1e9,
         }
-        c0 = sets[0][2].view(torch.uint8)
-        if first_c is None:
-            first_c = c0.clone()
-        elif not torch.equal(c0, first_c):
-            identical = False
-            print("# S=%d %s: C differs bitwise from the first pair" % (s, v), file=sys.stderr, flush=True)
-        print("# %-14s S=%d %-6s mean %8.2f us  %8.1f %s  %7.1f GB/s" % (
+        print("# %-14s S=%d %-6s median round %8.2f us  %8.1f %s  %7.1f GB/s  rounds %s" % (
             args.workload, s, v, mean * 1e3, results[(s, v)]["tops"],
-            "TOP/s" if dtype == "i8" else "TFLOP/s", results[(s, v)]["gbs"]), file=sys.stderr,
-            flush=True)
+            "TOP/s" if dtype == "i8" else "TFLOP/s", results[(s, v)]["gbs"],
+            " ".join("%.1f" % (x * 1e3) for x in rs)), file=sys.stderr, flush=True)
 
     best = min(results, key=lambda p: results[p]["mean_us"])
     r = results[best]
@@ -304,7 +319,9 @@ def main():
                    "lds_bytes": info["lds_bytes"], "grid": info["grid"], "splits": info["splits"]},
         "roofline": roof,
         "pairs_bit_identical": identical,
-        "sweep": {"S%d_%s" % p: {"us": q["mean_us"], "per_launch_median_us": q["median_us"],
+        "rounds": args.rounds,
+        "sweep": {"S%d_%s" % p: {"us": q["mean_us"], "rounds_us": q["rounds_us"],
+                                 "per_launch_median_us": q["median_us"],
                                  "per_launch_min_us": q["min_us"], "per_launch_max_us": q["max_us"],
                                  unit if bound != "hbm" else "GB/s":
                                      round(q["tops"] if bound != "hbm" else q["gbs"], 2),
