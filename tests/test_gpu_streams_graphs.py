@@ -1,0 +1,90 @@
+"""The C ABI on streams other than the default one, and inside a captured
+graph: gemm_run and gemm_run_splitk enqueue only kernel launches (no memory
+set-up or copies), so a graph that captures them replays them; the split-K
+arrival counters come back to zero after each replay.  Every replay runs on
+new inputs copied into the captured buffers (with eager work and
+synchronisation in between) and is checked against the oracle.
+"""
+import pytest
+import torch
+
+from software_pipelined_tiled_02_amd import binding, inputs
+from tests.gpu_util import check_close, oracle_full
+
+pytestmark = pytest.mark.gpu
+
+DIST = {"i8": "int", "f16": "normal", "bf16": "uniform", "f32": "uniform"}
+
+
+@pytest.fixture(scope="module")
+def g():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gg = binding.Gemm(0)
+    yield gg
+    gg.close()
+
+
+@pytest.mark.parametrize("dtype", ("i8", "bf16"))
+def test_side_stream(g, dtype):
+    M, N, K = 384, 320, 1008
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=31)
+    ref = oracle_full(a, b, dtype, "RC")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        da, db = a.cuda(), b.cuda()
+        c = torch.empty((M, N), dtype=inputs.OUT_TORCH_DTYPES[dtype], device="cuda")
+        binding.gemm_run(g.h, M, N, K, dtype, "RC", 2, "direct", da, K, db, K, c, N, stream=s)
+    s.synchronize()
+    check_close(c.cpu(), ref, dtype, "side stream")
+
+
+def _graph_case(g, dtype, splits, tile):
+    M, N, K = 384, 320, 2048
+    out_dt = inputs.OUT_TORCH_DTYPES[dtype]
+    g.set_tile(tile)
+    a0, b0 = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=0)
+    da, db = a0.cuda(), b0.cuda()
+    c = torch.zeros((M, N), dtype=out_dt, device="cuda")
+    _, info = binding.gemm_query(M, N, K, dtype, "RC", 3, "direct", tile=tile, splits=splits)
+    ws = g.workspace(info["workspace_bytes"]) if info["workspace_bytes"] else None
+
+    def call(stream):
+        if splits == 1:
+            binding.gemm_run(g.h, M, N, K, dtype, "RC", 3, "direct", da, K, db, K, c, N, stream=stream)
+        else:
+            binding.gemm_run_splitk(g.h, M, N, K, dtype, "RC", 3, "direct", splits, da, K, db, K, c, N,
+                                    ws, ws.numel(), stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side)                       # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream())
+    for rep in range(4):
+        a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=50 + rep)
+        da.copy_(a.cuda())
+        db.copy_(b.cuda())
+        c.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check_close(c.cpu(), oracle_full(a, b, dtype, "RC"), dtype,
+                    "%s graph replay %d (splits %d)" % (dtype, rep, splits))
+        _ = (da.float().sum() if dtype != "i8" else da.sum()).item()   # eager work between replays
+    if ws is not None:
+        assert int(ws[:65536].count_nonzero()) == 0
+    g.set_tile("auto")
+
+
+@pytest.mark.parametrize("dtype", ("i8", "f16"))
+def test_graph_replay(g, dtype):
+    _graph_case(g, dtype, 1, "auto")
+
+
+@pytest.mark.parametrize("dtype", ("i8", "bf16"))
+def test_graph_replay_splitk(g, dtype):
+    _graph_case(g, dtype, 4, "128x128")
