@@ -62,9 +62,10 @@
  *
  * Errors.  Every entry point returns GEMM_OK (0) or one of the codes below;
  * nothing is thrown across the ABI.  Argument checks run before any HIP call,
- * so a rejected call has no side effect.  gemm_run is asynchronous: it
- * enqueues on `stream` and returns; faults during execution surface at the
- * caller's next synchronisation of that stream.
+ * so a rejected call has no side effect.  gemm_run and gemm_run_splitk are
+ * asynchronous: each enqueues one kernel launch on `stream` (and nothing
+ * else, so a graph can capture it) and returns; faults during execution
+ * surface at the caller's next synchronisation of that stream.
  */
 #ifndef PIPEGEMM_H
 #define PIPEGEMM_H
@@ -86,8 +87,10 @@ enum {
     GEMM_ERR_ALIGNMENT = 2,    /* an alignment rule above is broken: C's, RR's N,
                                   A/B not element-aligned, or (direct variant
                                   only) A/B rows or K not whole 16-byte chunks */
-    GEMM_ERR_UNSUPPORTED = 3,  /* no kernel instance fits the LDS budget, or an
-                                  operand tile row span exceeds 2^31 bytes */
+    GEMM_ERR_UNSUPPORTED = 3,  /* no kernel instance fits the LDS budget, an
+                                  operand tile row span exceeds 2^31 bytes, or
+                                  (gemm_run_splitk) more than one split with
+                                  more than 16384 C tiles */
     GEMM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch
                                   failure); see gemm_last_hip_error */
 };

@@ -69,7 +69,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (has_c && ((C == nullptr && !query) || ldc < N)) return GEMM_ERR_INVALID_ARG;
     if (lda < 0 || ldb < 0 || ldc < 0) return GEMM_ERR_INVALID_ARG;
 
-    const int sz = pg::in_size(dtype), osz = pg::out_size(dtype), epc = pg::epc(dtype);
+    const int sz = pg::in_size(dtype), epc = pg::epc(dtype);
     // Operands: element-aligned always; 16-byte aligned rows (base, ld and K
     // whole 16-byte chunks) for the direct-to-LDS variant, whose loads write
     // LDS in whole 16-byte chunks.  The register-staged variant takes any K
@@ -163,7 +163,6 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     plan->kernel_variant = (variant == GEMM_VARIANT_REG && K % epc != 0) ? (int)pg::VAR_REG_KTAIL : variant;
     plan->tiles_m = tm;
     plan->tiles_n = tn;
-    (void)osz;
     return GEMM_OK;
 }
 
