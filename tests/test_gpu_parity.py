@@ -92,13 +92,23 @@ def test_padded_leading_dimensions(g, dtype, layout):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("layout", ("RR", "RC"))
-def test_identity_is_exact(g, dtype, layout):
-    """A = I gives C = B exactly at every dtype (one nonzero term per sum)."""
+@pytest.mark.parametrize("perm", (False, True))
+def test_identity_is_exact(g, dtype, layout, perm):
+    """A = I (or a permutation matrix) gives C = B (its rows permuted) exactly
+    at every dtype: one nonzero term per sum."""
     K = 8 * EPC[dtype] * 4 + EPC[dtype]          # ragged last tile
     M, N = K, 96
     _, b = inputs.make_operands(1, N, K, dtype, layout, DIST[dtype], seed=5)
-    a = torch.eye(M, K, dtype=torch.float32).to(inputs.TORCH_DTYPES[dtype])
+    a = torch.eye(M, K, dtype=torch.float32)
+    if perm:
+        a = a[torch.randperm(M, generator=torch.Generator().manual_seed(9))]
+    a = a.to(inputs.TORCH_DTYPES[dtype]).contiguous()
     ref = oracle_full(a, b, dtype, layout)
+    if perm:   # the oracle's C is B's rows permuted, with nothing added
+        rows = torch.argmax(a.float(), dim=1).numpy()
+        ref_b = oracle_full(torch.eye(K, K, dtype=torch.float32).to(inputs.TORCH_DTYPES[dtype]), b, dtype,
+                            layout)
+        assert np.array_equal(ref, ref_b[rows])
     for tile in ("auto", "128x128", "32x64"):
         g.set_tile(tile)
         for stages, variant in ((1, "reg"), (2, "direct"), (4, "direct"), (4, "reg")):
