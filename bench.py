@@ -30,6 +30,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -72,12 +73,17 @@ def flops(M, N, K):
 
 
 def kernel_source_hash():
+    """Hash of the library's sources with comments and white space removed,
+    so that only a change of code marks measured counters as stale."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_02_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".h", ".hip")) and not name.endswith("_probe.hip"):   # probes are no GEMM source
+            text = open(os.path.join(csrc, name), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,8 +13,9 @@
 //    tile boundary the wave waits with `s_waitcnt vmcnt(n)` until the next
 //    tile has landed (vmcnt counts this wave's outstanding loads, which
 //    retire in order -- the analogue of cp.async.wait_group), crosses one
-//    barrier, and refills the slot every wave has just finished reading.  STAGES = 1 is the serial
-//    load / sync / compute / sync loop of the README's Background section.
+//    barrier, and refills the slot every wave has just finished reading.
+//    STAGES = 1 is the serial load / sync / compute / sync loop of the
+//    README's Background section.
 //  * REG: buffer loads into VGPR staging sets, then ds_write_b128 into one
 //    of two LDS slots (ping-pong).  max(1, STAGES-1) staging sets keep that
 //    many tiles in flight in registers; STAGES = 1 is the skill's
@@ -40,8 +41,14 @@
 // (loaded in the prologue; see phys_tile), so it is the only load that
 // needs a per-lane test: its chunks past K get an offset beyond the
 // buffer's range, and an out-of-range buffer load returns 0 (also into
-// LDS).  Tiles past the last one get an out-of-range scalar offset and load
-// zeros.  Stores are masked.
+// LDS).  (When K is not whole 16-byte chunks -- register-staged instances
+// of their own -- the chunk holding column K-1 is read in exact pieces; see
+// load_k_tail.)  Tiles past the last one get an out-of-range scalar offset
+// and load zeros.  Stores are masked.
+//
+// Split K (splitk): the same kernel, given a split count above 1, runs one
+// K range of a C tile per workgroup and combines the partial tiles through
+// a workspace; with a split count of 1 it is the plain GEMM.
 #ifndef PIPEGEMM_GEMM_KERNEL_H
 #define PIPEGEMM_GEMM_KERNEL_H
 
@@ -152,7 +159,7 @@ struct Gemm {
     // ---- per-lane state --------------------------------------------------
     struct State {
         __amdgpu_buffer_rsrc_t ra, rb;
-        uint32_t offa[LA], offb[LB];   // byte offsets at K-tile 0 (kOob if the row is outside)
+        uint32_t offa[LA], offb[LB];   // byte offsets at K-tile 0 (rows past M or N: the tile's row 0)
         uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
         uint32_t rrb[RR ? FN : 1];     // layout RR: per-lane B fragment read offset (step 0)
@@ -392,8 +399,8 @@ struct Gemm {
         }
     }
 
-    // Load chunk j of logical K-tile kt (never tile 0): into LDS slot `slot`
-    // (DIRECT) or regs[j] (REG).
+    // Load chunk j of logical K-tile kt (never a head tile: those are all
+    // loaded in the prologue): into LDS slot `slot` (DIRECT) or regs[j] (REG).
     __device__ static __forceinline__ void load_one(const State& s, uint8_t PG_LDS* smem, int kt, int slot,
                                                     i32x4 (&regs)[LPT], int j) {
         if constexpr (VARIANT == VAR_DIRECT) {

@@ -57,3 +57,19 @@ def test_measured_ceiling_is_read_from_the_probe_output():
         assert c is not None and 0 < c <= bench.PEAK[dt], (dt, c)
     h = bench.measured_ceiling("bf16", "hbm")
     assert h is not None and 0 < h <= bench.HBM_PEAK_GBS
+
+
+def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
+    """Only a change of code, not of comments or spacing, changes the hash."""
+    import shutil
+    src = os.path.join(ROOT, "software_pipelined_tiled_02_amd", "csrc")
+    root = tmp_path / "r"
+    shutil.copytree(src, root / "software_pipelined_tiled_02_amd" / "csrc")
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    h0 = bench.kernel_source_hash()
+    f = root / "software_pipelined_tiled_02_amd" / "csrc" / "tile_layout.h"
+    text = f.read_text()
+    f.write_text("// a new comment\n/* and a block\n comment */\n" + text.replace("\n", "\n\n", 3))
+    assert bench.kernel_source_hash() == h0
+    f.write_text(text.replace("constexpr int kChunk = 16;", "constexpr int kChunk = 32;"))
+    assert bench.kernel_source_hash() != h0
