@@ -181,8 +181,22 @@ struct Gemm {
     // `rot`.  The head is defined by BKMAX rather than BK so that instances
     // with BK = BKMAX / 2 add the same k-slices in the same order, and every
     // (stages, variant) pair gives bit-identical C.
+    // Register-staged instances compute it with masks: written as
+    // conditionals, the compiler made branches of them that split the main
+    // loop's scheduled steps, and its waits at the joins cost up to 20%.  The
+    // direct instances keep the conditionals: with masks the compiler copied
+    // the loop-carried fragments in the 3-4 stage 256x256 loops (16 moves
+    // per K-tile, 6% slower), which it does not do with these.  Both forms
+    // compute the same tile.
     __device__ static __forceinline__ int phys_tile(const State& s, int t) {
-        return t < s.head ? s.tail0 + t : s.tbase + k_phys_tile(t, s.head, s.nbody, s.rot);
+        if constexpr (VARIANT == VAR_DIRECT) {
+            return t < s.head ? s.tail0 + t : s.tbase + k_phys_tile(t, s.head, s.nbody, s.rot);
+        } else {
+            const int b = t - s.head + s.rot;                                // body position, before the wrap
+            const int body = s.tbase + b - (s.nbody & -(int)(b >= s.nbody)); // = tbase + k_phys_tile(...)
+            const int in_head = -(int)(t < s.head);
+            return ((s.tail0 + t) & in_head) | (body & ~in_head);
+        }
     }
     // Scalar (wave-uniform) byte offset of logical K-tile t; past the last
     // tile, an offset that takes every lane out of the buffer's range.
@@ -190,10 +204,16 @@ struct Gemm {
     // -- so that the compiler keeps the offset in a scalar register instead
     // of looping over lanes.)
     __device__ static __forceinline__ uint32_t soff_a(const State& s, int t) {
-        return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ) : kOob);
+        if constexpr (VARIANT == VAR_DIRECT)
+            return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ) : kOob);
+        const uint32_t past = kOob & (uint32_t)-(int)(t >= s.nt);
+        return __builtin_amdgcn_readfirstlane(((uint32_t)phys_tile(s, t) * (uint32_t)(BK * SZ)) | past);
     }
     __device__ static __forceinline__ uint32_t soff_b(const State& s, int t) {
-        return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob);
+        if constexpr (VARIANT == VAR_DIRECT)
+            return __builtin_amdgcn_readfirstlane(t < s.nt ? (uint32_t)phys_tile(s, t) * s.kb_step : kOob);
+        const uint32_t past = kOob & (uint32_t)-(int)(t >= s.nt);
+        return __builtin_amdgcn_readfirstlane(((uint32_t)phys_tile(s, t) * s.kb_step) | past);
     }
     // Per-lane offset of chunk j.  FIRST: the chunk belongs to the last
     // physical K-tile (logical tile head-1), which may be ragged; chunks
@@ -379,6 +399,13 @@ struct Gemm {
     static constexpr int NU = FM * FN;      // units per step
     static constexpr int NRU = FM + FN;     // fragment reads per step (A-side first)
     static constexpr int HALF = LPT / 2;    // loads issued right after the barrier
+    // Where a step forms its loads' scalar offsets: once at its start (the
+    // 256x256 classes) or at each load (the others).  Same instructions,
+    // placed differently; measured, each placement is the one whose loop
+    // the compiler keeps in one piece with the fewest waits: the other cost
+    // 13% in the 3-stage 256x256 direct loop (a branch inside it) and 3% in
+    // the 32x64 one (a wait before every MFMA).
+    static constexpr bool HOIST_SOFF = BM == 256;
     static constexpr int LSTEPS = KSTEPS - 1 < 2 ? KSTEPS - 1 : 2;   // body steps carrying the rest
     static constexpr int rd_lo(int u) { return u * ((NRU + NU - 1) / NU) < NRU ? u * ((NRU + NU - 1) / NU) : NRU; }
 
@@ -401,20 +428,25 @@ struct Gemm {
 
     // Load chunk j of logical K-tile kt (never a head tile: those are all
     // loaded in the prologue): into LDS slot `slot` (DIRECT) or regs[j] (REG).
-    __device__ static __forceinline__ void load_one(const State& s, uint8_t PG_LDS* smem, int kt, int slot,
-                                                    i32x4 (&regs)[LPT], int j) {
+    // sa / sb: the K-tile's scalar offsets when the caller computed them
+    // (HOIST_SOFF), else computed here.
+    __device__ static __forceinline__ void load_one(const State& s, uint8_t PG_LDS* smem, int kt, uint32_t sa,
+                                                    uint32_t sb, int slot, i32x4 (&regs)[LPT], int j) {
+        if constexpr (!HOIST_SOFF) {
+            sa = soff_a(s, kt);
+            sb = soff_b(s, kt);
+        }
         if constexpr (VARIANT == VAR_DIRECT) {
             uint8_t PG_LDS* base = smem + slot * SLOT;
             if (j < LA)
-                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, s.offa[j], soff_a(s, kt));
+                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, s.offa[j], sa);
             else
-                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, s.offb[j - LA],
-                        soff_b(s, kt));
+                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, s.offb[j - LA], sb);
         } else {
             if (j < LA)
-                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.offa[j], soff_a(s, kt), 0);
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.offa[j], sa, 0);
             else
-                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.offb[j - LA], soff_b(s, kt), 0);
+                regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.rb, s.offb[j - LA], sb, 0);
         }
     }
 
@@ -427,6 +459,13 @@ struct Gemm {
                                                 Frags& nxt, int rd_slot, int rd_st, acc_t (&acc)[FM][FN],
                                                 int J0, int J1, int ld_kt, int ld_slot, i32x4 (&regs)[LPT]) {
         const int NL = J1 - J0;
+        uint32_t ld_sa = 0, ld_sb = 0;
+        if constexpr (HOIST_SOFF) {
+            if (NL > 0) {
+                ld_sa = soff_a(s, ld_kt);
+                ld_sb = soff_b(s, ld_kt);
+            }
+        }
         if constexpr (RR && SZ != 4 && VARIANT == VAR_DIRECT) {
             // the transposing reads of `cur` (inline assembly) have landed
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
@@ -441,7 +480,7 @@ struct Gemm {
             }
 #pragma unroll
             for (int j = J0 + u * NL / NU; j < J0 + (u + 1) * NL / NU; ++j)
-                load_one(s, smem, ld_kt, ld_slot, regs, j);
+                load_one(s, smem, ld_kt, ld_sa, ld_sb, ld_slot, regs, j);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -621,15 +660,23 @@ struct Gemm {
             s.tbase = u0 * per;
             s.tail0 = units * per;
             s.klast = (uint32_t)(units * per + head - 1) * BK;
+            // Start the K loop of the tiles on XCD x at unit 9x (mod the
+            // count): with every XCD reading the same K columns at once, the
+            // row-strided reads pile onto the same HBM channels (measured on
+            // the skinny 8192x64x8192 shape: 4.0 -> 4.5 TB/s; on 8192^2 x
+            // 8200 with 256x256 tiles, 3-7% at every stage count).  Within an
+            // XCD the tiles keep a common K position, so they still share
+            // operands in its L2.  The 256x256 tiles rotate only when the
+            // workgroups loop over more work than one pass (operands then
+            // stream from HBM): with one tile per CU (4096^3, operands held
+            // in the Infinity Cache) XCDs that share A rows gain from
+            // reading them together, and rotating cost the 3-4 stage
+            // instances 6%.  Counted in BKMAX units, so every stage count
+            // starts at the same k-slice; every (stages, variant) pair of a
+            // call takes the same decision.
+            const bool rotate = BM < 256 || args.tiles_m * args.tiles_n * args.splits > (int)gridDim.x;
+            s.rot = (rotate && u1 > u0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)(u1 - u0)) * per : 0;
         }
-        // Start the K loop of the tiles on XCD x at full tile 9x (mod the
-        // count): with every XCD reading the same K columns at once, the
-        // row-strided reads of A pile onto the same HBM channels (measured on
-        // the skinny 8192x64x8192 shape: 4.0 -> 4.5 TB/s).  Within an XCD the
-        // tiles keep a common K position, so they still share B in its L2.
-        // The 256x256 tiles keep the plain order: their bands share A and B
-        // across each XCD's tiles and gain nothing from it.
-        s.rot = (BM < 256 && s.nbody > 0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)s.nbody) : 0;
         const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
         const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
                               : (const uint8_t*)args.B + (int64_t)n0 * args.ldb * SZ;

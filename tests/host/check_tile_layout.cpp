@@ -144,6 +144,48 @@ int main() {
         }
     std::printf("K-tile order: %s\n", order_fail ? "FAIL" : "permutation, ragged tile loaded first, one k-slice order for all stage counts");
     fail += order_fail;
+
+    // The kernel's order with K split into P ranges of whole bkmax units
+    // (the ragged head with the last split) and each range started at unit
+    // rot_u: logical tile t of split p is physical tile tail0 + t for
+    // t < head, else tbase + k_phys_tile(t, head, nbody, rot_u * per).
+    // Every (P, rot_u): the splits together cover each physical tile once,
+    // and the 1-stage and 3-stage K-tiles add the same k-slices in one order.
+    int split_fail = 0;
+    for (int dt = 0; dt < 4; ++dt)
+        for (int tc = 0; tc < TILE_COUNT; ++tc) {
+            const int bkmax = block_k(dt, tc, 1), slice = 2 * epc(dt);
+            for (int K = 1; K <= 9 * bkmax; K += (K < 3 * bkmax ? 5 : 11))
+                for (int P = 1; P <= 3; ++P)
+                    for (int rot_u = 0; rot_u < 9; rot_u += 4) {
+                        int seq[2][1024], len[2] = {0, 0};
+                        for (int si = 0; si < 2; ++si) {
+                            const int s = si == 0 ? 1 : 3, bk = block_k(dt, tc, s), per = bkmax / bk;
+                            const int nt = (K + bk - 1) / bk, units = K / bkmax, head = k_head_tiles(K, bk, bkmax);
+                            bool seen[2048] = {false};
+                            int covered = 0;
+                            for (int p = 0; p < P; ++p) {
+                                const int u0 = p * units / P, u1 = (p + 1) * units / P;
+                                const int hd = p == P - 1 ? head : 0, nbody = (u1 - u0) * per;
+                                const int rot = u1 > u0 ? (rot_u % (u1 - u0)) * per : 0;
+                                for (int t = 0; t < nbody + hd; ++t) {
+                                    const int q = t < hd ? units * per + t : u0 * per + k_phys_tile(t, hd, nbody, rot);
+                                    if (q < 0 || q >= nt || seen[q]) { ++split_fail; continue; }
+                                    seen[q] = true;
+                                    ++covered;
+                                    for (int k0 = q * bk; k0 < (q + 1) * bk; k0 += slice)
+                                        if (k0 < K && len[si] < 1024) seq[si][len[si]++] = k0;
+                                }
+                            }
+                            if (covered != nt) ++split_fail;
+                        }
+                        if (len[0] != len[1]) ++split_fail;
+                        for (int i = 0; i < len[0] && i < len[1]; ++i)
+                            if (seq[0][i] != seq[1][i]) { ++split_fail; break; }
+                    }
+        }
+    std::printf("K splits and rotation: %s\n", split_fail ? "FAIL" : "every tile once, one k-slice order for all stage counts");
+    fail += split_fail;
     std::printf(fail ? "FAIL (%d)\n" : "OK\n", fail);
     return fail ? 1 : 0;
 }
