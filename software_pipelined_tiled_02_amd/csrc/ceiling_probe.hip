@@ -8,10 +8,14 @@
 // 4 x 4 blocks of 32 x 32 accumulators and, per k-step, reads 8 operand
 // fragments (16 bytes per lane) from an LDS buffer of random values and
 // issues the 16 MFMAs of the step -- the GEMM's ratio of LDS reads to MFMAs,
-// without global memory traffic.  The data are random because the MFMA's
-// power draw, and with it the clock the chip holds, depends on the operand
-// bits; the effective clock is reported from s_memtime against the fixed
-// 100 MHz s_memrealtime.
+// without global memory traffic.  As in the GEMM, a step's fragments are read
+// during the previous step's MFMAs, so LDS latency stays hidden.  A second
+// figure per type (suffix _regs) feeds the MFMAs from two register-resident
+// fragment sets used in turn, without LDS reads.  The data are random
+// because the MFMA's power draw, and with it the clock the chip holds,
+// depends on the operand bits; the effective clock is reported from
+// s_memtime against the fixed 100 MHz s_memrealtime, and with it the share of
+// cycles the matrix cores are busy (rate / (per-clock datasheet rate x clock)).
 //
 // HBM ceiling.  A 1 GiB buffer (four times the Infinity Cache) read once with
 // 16-byte loads, each workgroup sweeping one contiguous block; and the same
@@ -77,7 +81,32 @@ __device__ __forceinline__ i32x4 random_unit(int dt, uint32_t i, uint32_t b) {
     return v;
 }
 
-template <int DT>
+// One k-step of a wave: the 16 MFMAs on fragments (x, y); with FEED, the
+// next step's 8 fragments are read from LDS into (nx, ny), one after each of
+// the first 8 MFMAs, while the matrix core works -- the GEMM's two-deep
+// register pipeline, so no MFMA waits on a read issued in the same step.
+template <int DT, bool FEED>
+__device__ __forceinline__ void probe_step(typename Acc<DT>::type (&acc)[4][4], const i32x4 (&x)[4],
+                                           const i32x4 (&y)[4], i32x4 (&nx)[4], i32x4 (&ny)[4],
+                                           const i32x4 LDSP* lds, int next, int lane) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        acc[u / 4][u % 4] = mma<DT>(x[u % 4], y[u / 4], acc[u / 4][u % 4]);
+        if (FEED && u < 8) {
+            // unit index < 64 * 64 = kLdsUnits
+            const int r = u & 3;
+            if (u < 4) nx[r] = lds[((next * 8 + r) & 63) * 64 + lane];
+            else ny[r] = lds[((next * 8 + 4 + r) & 63) * 64 + lane];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// FEED: every k-step's operands come from LDS (random values), read one step
+// ahead.  Without FEED the operands are two random fragment sets read once
+// and used in turn: the matrix core alone, with operand bits that still
+// change every step.
+template <int DT, bool FEED>
 __global__ void __launch_bounds__(256) mfma_ceiling(int iters, int* out, unsigned long long* clk) {
     typedef typename Acc<DT>::type acc_t;
     __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsUnits * 16];
@@ -85,23 +114,22 @@ __global__ void __launch_bounds__(256) mfma_ceiling(int iters, int* out, unsigne
     const int tid = threadIdx.x, lane = tid & 63;
     for (int i = tid; i < kLdsUnits; i += 256) lds[i] = random_unit(DT, (uint32_t)i, blockIdx.x);
     __syncthreads();
-    const unsigned long long t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
     acc_t acc[4][4];
     for (int a = 0; a < 4; ++a)
         for (int b = 0; b < 4; ++b)
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0;
-    for (int it = 0; it < iters; ++it) {
-        i32x4 x[4], y[4];
+    i32x4 x0[4], y0[4], x1[4], y1[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            // unit index < 64 * 64 = kLdsUnits
-            x[a] = lds[((it * 8 + a) & 63) * 64 + lane];
-            y[a] = lds[((it * 8 + 4 + a) & 63) * 64 + lane];
-        }
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = mma<DT>(x[b], y[a], acc[a][b]);
+    for (int a = 0; a < 4; ++a) {
+        x0[a] = lds[a * 64 + lane];
+        y0[a] = lds[(4 + a) * 64 + lane];
+        x1[a] = lds[(8 + a) * 64 + lane];
+        y1[a] = lds[(12 + a) * 64 + lane];
+    }
+    const unsigned long long t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; it += 2) {   // iters is even
+        probe_step<DT, FEED>(acc, x0, y0, x1, y1, lds, it + 1, lane);
+        probe_step<DT, FEED>(acc, x1, y1, x0, y0, lds, it + 2, lane);
     }
     const unsigned long long t1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
     int s = 0;
@@ -149,7 +177,7 @@ __global__ void __launch_bounds__(256) hbm_copy(const i32x4* __restrict__ src, i
         }                                                                        \
     } while (0)
 
-template <int DT>
+template <int DT, bool FEED>
 int run_mfma(const char* name, double peak, int cus) {
     int* out;
     unsigned long long* clk;
@@ -159,11 +187,11 @@ int run_mfma(const char* name, double peak, int cus) {
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
-    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(mfma_ceiling<DT>, dim3(cus), dim3(256), 0, 0, iters, out, clk);
+    for (int w = 0; w < 3; ++w) mfma_ceiling<DT, FEED><<<dim3(cus), dim3(256)>>>(iters, out, clk);
     CHECK(hipDeviceSynchronize());
     CHECK(hipEventRecord(e0));
     const int reps = 5;
-    for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(mfma_ceiling<DT>, dim3(cus), dim3(256), 0, 0, iters, out, clk);
+    for (int r = 0; r < reps; ++r) mfma_ceiling<DT, FEED><<<dim3(cus), dim3(256)>>>(iters, out, clk);
     CHECK(hipEventRecord(e1));
     CHECK(hipEventSynchronize(e1));
     float ms;
@@ -180,8 +208,11 @@ int run_mfma(const char* name, double peak, int cus) {
     // per wave and iteration: 16 blocks of 32 x 32 x chunk_k multiply-adds
     const double ops = 2.0 * 16 * 32 * 32 * chunk_k<DT>() * 4 * (double)cus * iters;
     const double t = ops / (ms * 1e-3) / 1e12;
-    std::printf("mfma_%s: %.1f %s, effective clock %.3f GHz, %.1f%% of the %.1f datasheet peak\n", name, t,
-                DT == I8 ? "TOP/s" : "TFLOP/s", ghz, 100.0 * t / peak, peak);
+    // matrix-core busy share: the rate against the datasheet's per-clock rate at the measured clock
+    const double busy = t / (peak * ghz / 2.4);
+    std::printf("mfma_%s%s: %.1f %s, effective clock %.3f GHz, %.1f%% of the %.1f datasheet peak, "
+                "matrix cores busy %.1f%% of cycles\n", name, FEED ? "" : "_regs", t,
+                DT == I8 ? "TOP/s" : "TFLOP/s", ghz, 100.0 * t / peak, peak, 100.0 * busy);
     CHECK(hipFree(out));
     CHECK(hipFree(clk));
     return 0;
@@ -194,8 +225,11 @@ int main() {
     CHECK(hipGetDevice(&dev));
     CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     std::printf("compute_units: %d\n", cus);
-    if (run_mfma<I8>("int8", 5033.2, cus) || run_mfma<F16>("fp16", 2516.6, cus) ||
-        run_mfma<BF16>("bf16", 2516.6, cus) || run_mfma<F32>("fp32", 157.3, cus))
+    if (run_mfma<I8, true>("int8", 5033.2, cus) || run_mfma<F16, true>("fp16", 2516.6, cus) ||
+        run_mfma<BF16, true>("bf16", 2516.6, cus) || run_mfma<F32, true>("fp32", 157.3, cus))
+        return 1;
+    if (run_mfma<I8, false>("int8", 5033.2, cus) || run_mfma<F16, false>("fp16", 2516.6, cus) ||
+        run_mfma<BF16, false>("bf16", 2516.6, cus))
         return 1;
 
     const uint64_t bytes = (uint64_t)1 << 30;
