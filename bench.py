@@ -118,6 +118,17 @@ def measured_ceiling(dtype, bound):
     return None
 
 
+def host_cpu():
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(M, N, K, dtype, layout, dist, scale, target_s):
     """The oracle, untuned, on a bounded row sample of the same workload."""
     import oracle
@@ -138,7 +149,7 @@ def cpu_baseline(M, N, K, dtype, layout, dist, scale, target_s):
             "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
             "cores": orc.num_threads(), "kind": "oracle",
             "sample": "first %d of %d rows of C (%dx%dx%d), %.1f s wall, host %s" % (
-                rows, M, rows, N, K, el, platform.processor() or platform.machine())}
+                rows, M, rows, N, K, el, host_cpu())}
 
 
 def main():

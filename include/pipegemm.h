@@ -46,6 +46,10 @@
  *     README's cp.async case; here the LDS-DMA form of buffer loads).  An
  *     LDS ring of `stages` slots with stages-1 tiles in flight; stages = 1 is
  *     the serial load-sync-compute-sync loop of the README's Background.
+ *     The 256x256 tiles keep their full K-tile at stages = 3 by splitting
+ *     the ring by operand: three slots for A (two tiles in flight), two for
+ *     B (one in flight), 160 KiB in all; at stages = 4 they halve the
+ *     K-tile (four whole slots).
  *   GEMM_VARIANT_REG: global -> VGPR -> LDS (the README's ping-pong case).
  *     min(stages, 2) LDS slots and max(1, stages-1) register staging sets,
  *     each a tile in flight; stages = 1 is the skill's register-only prefetch
@@ -111,9 +115,12 @@ typedef struct {
     int32_t block_m, block_n, block_k;
     int32_t waves_m, waves_n;
     int32_t threads;         /* per workgroup */
-    int32_t lds_slots;       /* slots of the LDS ring */
+    int32_t lds_slots;       /* slots of the LDS ring (the split ring of
+                                the 256x256 tiles at 3 direct stages: 3 for
+                                A, 2 for B) */
     int32_t reg_sets;        /* VGPR staging sets (0 for the direct variant) */
-    int32_t tiles_in_flight; /* K-tiles loading while one is multiplied */
+    int32_t tiles_in_flight; /* K-tiles loading while one is multiplied
+                                (split ring: 2 for A, 1 for B) */
     int32_t lds_bytes;       /* LDS per workgroup */
     int32_t loads_per_tile;  /* 16-byte loads per lane per K-tile */
     int64_t grid;            /* workgroups launched */

@@ -101,7 +101,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (!pg::instance_fits(dtype, tc, stages, variant)) return GEMM_ERR_UNSUPPORTED;
 
     const pg::TileShape ts = pg::tile_shape(tc);
-    const int bk = pg::block_k(dtype, tc, stages);
+    const int bk = pg::block_k(dtype, tc, stages, variant);
     // 32-bit buffer offsets: one workgroup's operand rows (and, for a
     // row-major B, the whole K extent) must stay below 2^31 bytes.
     const int64_t lim = (int64_t)1 << 31;
@@ -125,7 +125,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.reg_sets = pg::reg_sets(variant, stages);
     in.tiles_in_flight = pg::tiles_in_flight(variant, stages);
     in.lds_bytes = pg::lds_bytes(dtype, tc, stages, variant);
-    in.loads_per_tile = pg::loads_a(dtype, tc, stages) + pg::loads_b(dtype, tc, stages);
+    in.loads_per_tile = pg::loads_a(dtype, tc, stages, variant) + pg::loads_b(dtype, tc, stages, variant);
     // The 256x256 tiles run one workgroup per CU (their LDS ring and
     // registers allow no second one); with more tiles than CUs, a grid of
     // one workgroup per CU loops over the tiles, so that one tile's C stores
@@ -138,7 +138,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     // split count (measured on 1024 x 1024 x 8192 bf16 with 256 x 256
     // tiles: 177 us at 8 splits, 320 us at 16, against 45 us for 128 x 128
     // tiles at 4).
-    const int64_t units = K / pg::block_k(dtype, tc, 1);
+    const int64_t units = K / pg::block_k(dtype, tc, 1, variant);
     int64_t P = splits;
     if (P == 0) {
         P = (tm * tn > 0 && tm * tn < num_cus) ? ceil_div(num_cus, tm * tn) : 1;

@@ -15,7 +15,10 @@
 //    retire in order -- the analogue of cp.async.wait_group), crosses one
 //    barrier, and refills the slot every wave has just finished reading.
 //    STAGES = 1 is the serial load / sync / compute / sync loop of the
-//    README's Background section.
+//    README's Background section.  At 3 stages the 256x256 classes split the
+//    ring by operand (three A slots, two B slots; see split_ring): the A tile
+//    of K-tile kt+2 is loaded while tile kt is multiplied, the B tile of
+//    kt+2 right after the barrier that ends tile kt.
 //  * REG: buffer loads into VGPR staging sets, then ds_write_b128 into one
 //    of two LDS slots (ping-pong).  max(1, STAGES-1) staging sets keep that
 //    many tiles in flight in registers; STAGES = 1 is the skill's
@@ -131,12 +134,12 @@ struct Gemm {
     static constexpr int BM = TS.bm, BN = TS.bn, WM = TS.wm, WN = TS.wn;
     static constexpr int T = WM * WN * 64;
     static constexpr int SZ = in_size(DT), OSZ = out_size(DT), EPC = epc(DT);
-    static constexpr int CPR = cpr_k(TC, STAGES);          // chunks per K-contiguous row
+    static constexpr int CPR = cpr_k(TC, STAGES, VARIANT); // chunks per K-contiguous row
     static constexpr int BK = CPR * EPC;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KSTEPS = CPR / 2;                  // two chunks per MFMA step
-    static constexpr int LA = loads_a(DT, TC, STAGES), LB = loads_b(DT, TC, STAGES);
+    static constexpr int LA = loads_a(DT, TC, STAGES, VARIANT), LB = loads_b(DT, TC, STAGES, VARIANT);
     static constexpr int LPT = LA + LB;
     static constexpr int A_BYTES = BM * CPR * kChunk;
     static constexpr int B_BYTES = BN * BK * SZ;
@@ -145,6 +148,7 @@ struct Gemm {
     static constexpr int RSETS = reg_sets(VARIANT, STAGES);
     static constexpr int LDS = lds_bytes(DT, TC, STAGES, VARIANT);   // the ring, or the epilogue strips
     static constexpr bool RR = (LAYOUT == LAYOUT_RR);
+    static constexpr bool SPLIT = split_ring(TC, STAGES, VARIANT);   // three A slots, two B slots
     static constexpr int CPR_BRR = BN * SZ / kChunk;       // chunks per row of a K x N B tile
     static constexpr int RB_RR = BN * SZ;                   // bytes per row of a K x N B tile
     typedef typename AccT<DT>::type acc_t;
@@ -235,14 +239,15 @@ struct Gemm {
     // writes in; the lane's source chunk is the logical one stored there.
     template <int J0, int J1, bool FIRST = false>
     __device__ static __forceinline__ void issue_direct(const State& s, uint8_t PG_LDS* smem, int kt, int slot) {
-        uint8_t PG_LDS* base = smem + slot * SLOT;
+        uint8_t PG_LDS* abase = smem + a_off(slot);
+        uint8_t PG_LDS* bbase = smem + b_off(slot);
         const uint32_t sa = soff_a(s, kt), sb = soff_b(s, kt);
 #pragma unroll
         for (int j = J0; j < J1; ++j) {
             if (j < LA)
-                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, voff_a<FIRST>(s, j), sa);
+                lds_dma(s, true, abase + (j * T + 64 * s.wave) * kChunk, voff_a<FIRST>(s, j), sa);
             else
-                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, voff_b<FIRST>(s, j - LA), sb);
+                lds_dma(s, false, bbase + ((j - LA) * T + 64 * s.wave) * kChunk, voff_b<FIRST>(s, j - LA), sb);
         }
     }
 
@@ -382,8 +387,16 @@ struct Gemm {
         i32x4 x[FN];
     };
 
-    __device__ static __forceinline__ const uint8_t PG_LDS* slot_ptr(const uint8_t PG_LDS* smem, int slot) {
-        return smem + slot * SLOT;
+    // Byte offsets of the A and B tiles of ring slot `slot`.  Split ring:
+    // `slot` is the K-tile index mod 6; its A tile is in A slot slot % 3
+    // (the first 3 * A_BYTES of LDS), its B tile in B slot slot % 2.
+    __device__ static __forceinline__ uint32_t a_off(int slot) {
+        if constexpr (SPLIT) return (uint32_t)(slot - 3 * (int)(slot >= 3)) * A_BYTES;
+        else return (uint32_t)slot * SLOT;
+    }
+    __device__ static __forceinline__ uint32_t b_off(int slot) {
+        if constexpr (SPLIT) return 3u * A_BYTES + (uint32_t)(slot & 1) * B_BYTES;
+        else return (uint32_t)slot * SLOT + A_BYTES;
     }
 
     // ---- the MFMA step schedule -------------------------------------------
@@ -412,8 +425,8 @@ struct Gemm {
     // Fragment read r of step st of the K-tile in `slot`.
     __device__ static __forceinline__ void read_one(const State& s, const uint8_t PG_LDS* smem, int slot,
                                                     int st, int r, Frags& f) {
-        const uint8_t PG_LDS* as = slot_ptr(smem, slot);
-        const uint8_t PG_LDS* bs = as + A_BYTES;
+        const uint8_t PG_LDS* as = smem + a_off(slot);
+        const uint8_t PG_LDS* bs = smem + b_off(slot);
         const int lane = s.tid & 63;
         if (r < FM) {
             f.y[r] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + r * 32) * CPR * kChunk + s.rd[st]);
@@ -437,11 +450,10 @@ struct Gemm {
             sb = soff_b(s, kt);
         }
         if constexpr (VARIANT == VAR_DIRECT) {
-            uint8_t PG_LDS* base = smem + slot * SLOT;
             if (j < LA)
-                lds_dma(s, true, base + (j * T + 64 * s.wave) * kChunk, s.offa[j], sa);
+                lds_dma(s, true, smem + a_off(slot) + (j * T + 64 * s.wave) * kChunk, s.offa[j], sa);
             else
-                lds_dma(s, false, base + A_BYTES + ((j - LA) * T + 64 * s.wave) * kChunk, s.offb[j - LA], sb);
+                lds_dma(s, false, smem + b_off(slot) + ((j - LA) * T + 64 * s.wave) * kChunk, s.offb[j - LA], sb);
         } else {
             if (j < LA)
                 regs[j] = __builtin_amdgcn_raw_buffer_load_b128(s.ra, s.offa[j], sa, 0);
@@ -489,18 +501,21 @@ struct Gemm {
     // 0's fragments; each step reads the next step's while its MFMAs run (a
     // two-deep register pipeline).  When LOADS, the first LSTEPS steps also
     // carry chunks [HALF, LPT) of K-tile ld_kt (the chunks [0, HALF) went out
-    // right after the previous barrier).  KSTEPS is even, so on exit f[1]
-    // holds the last step's fragments and f[0] is free for the next tile.
+    // right after the previous barrier); in a split ring, its A chunks
+    // [0, LA) (its B chunks follow the next barrier).  KSTEPS is even, so on
+    // exit f[1] holds the last step's fragments and f[0] is free for the next
+    // tile.
     template <bool LOADS>
     __device__ static __forceinline__ void tile_body(const State& s, uint8_t PG_LDS* smem, int slot,
                                                      Frags (&f)[2], acc_t (&acc)[FM][FN], int ld_kt,
                                                      int ld_slot, i32x4 (&regs)[LPT]) {
         static_assert(KSTEPS % 2 == 0, "step parity");
-        constexpr int REST = LPT - HALF;
+        constexpr int BJ0 = SPLIT ? 0 : HALF, BJ1 = SPLIT ? LA : LPT;   // chunks the body carries
+        constexpr int REST = BJ1 - BJ0;
 #pragma unroll
         for (int st = 0; st + 1 < KSTEPS; ++st) {
-            const int j0 = (LOADS && st < LSTEPS) ? HALF + st * REST / LSTEPS : 0;
-            const int j1 = (LOADS && st < LSTEPS) ? HALF + (st + 1) * REST / LSTEPS : 0;
+            const int j0 = (LOADS && st < LSTEPS) ? BJ0 + st * REST / LSTEPS : 0;
+            const int j1 = (LOADS && st < LSTEPS) ? BJ0 + (st + 1) * REST / LSTEPS : 0;
             step<true>(s, smem, f[st & 1], f[(st + 1) & 1], slot, st + 1, acc, j0, j1, ld_kt, ld_slot, regs);
         }
     }
@@ -649,7 +664,7 @@ struct Gemm {
             // K splits are whole BKMAX-wide units, so that every stage count
             // adds the same k-slices in the same order; the ragged head goes
             // with the last split.
-            constexpr int BKMAX = block_k(DT, TC, 1);
+            constexpr int BKMAX = block_k(DT, TC, 1, VARIANT);
             static_assert(BKMAX % BK == 0 && (BKMAX == BK || STAGES >= 3), "head tiles are all in the prologue");
             const int head = k_head_tiles(args.K, BK, BKMAX);
             const int units = args.K / BKMAX, per = BKMAX / BK;
@@ -778,22 +793,29 @@ struct Gemm {
         } else if constexpr (VARIANT == VAR_DIRECT) {
             // Ring of STAGES slots: while tile kt is multiplied, tiles
             // kt+1 .. kt+STAGES-1 are in flight; tile kt+STAGES-1 goes into
-            // the slot tile kt-1 used.
+            // the slot tile kt-1 used.  Split ring (slots counted mod 6):
+            // while tile kt is multiplied, the A tile of kt+2 goes into the A
+            // slot tile kt-1 used; after the barrier that ends tile kt, the B
+            // tile of kt+2 goes into the B slot tile kt used.  At that
+            // barrier only the A tile of kt+2 may still be in flight.
             i32x4 none[LPT];
+            constexpr int NSLOT = SPLIT ? 6 : STAGES;
+            constexpr int WAITN = SPLIT ? LA : (STAGES - 2) * LPT;
+            constexpr int HJ0 = SPLIT ? LA : 0, HJ1 = SPLIT ? LPT : HALF, HKT = SPLIT ? 2 : STAGES;
 #pragma unroll
             for (int t = 0; t < STAGES - 1; ++t) first_direct(s, smem, t, t);
             wait_vmcnt<(STAGES - 2) * LPT>();
             block_sync();
             read_first(s, smem, 0, f[0]);
-            issue_direct<0, HALF>(s, smem, STAGES - 1, STAGES - 1);
+            if constexpr (!SPLIT) issue_direct<0, HALF>(s, smem, STAGES - 1, STAGES - 1);
             int slot = 0;
             for (int kt = 0; kt < nt; ++kt) {
-                const int prev = (slot == 0) ? STAGES - 1 : slot - 1;
-                const int next = (slot + 1 == STAGES) ? 0 : slot + 1;
+                const int prev = (slot == 0) ? NSLOT - 1 : slot - 1;
+                const int next = (slot + 1 == NSLOT) ? 0 : slot + 1;
                 tile_body<true>(s, smem, slot, f, acc, kt + STAGES - 1, prev, none);
-                wait_vmcnt<(STAGES - 2) * LPT>();     // tile kt+1 landed (this wave)
+                wait_vmcnt<WAITN>();                 // tile kt+1 landed (this wave)
                 block_sync();                        // ...all waves; slot of kt free
-                step<true>(s, smem, f[1], f[0], next, 0, acc, 0, HALF, kt + STAGES, slot, none);
+                step<true>(s, smem, f[1], f[0], next, 0, acc, HJ0, HJ1, kt + HKT, slot, none);
                 slot = next;
             }
             wait_vmcnt<0>();   // no LDS write may outlive the loop
@@ -901,7 +923,8 @@ struct Gemm {
     static constexpr int LANES_PER_ROW = WTN * OSZ / kChunk;
     static constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
     static_assert(64 % LANES_PER_ROW == 0 && 32 % ROWS_PER_STORE == 0, "epilogue store shape");
-    static_assert(STRIP_BYTES * WM * WN <= LDS && SLOT * SLOTS <= LDS, "LDS layout");
+    static_assert(STRIP_BYTES * WM * WN <= LDS && (SPLIT ? 3 * A_BYTES + 2 * B_BYTES : SLOT * SLOTS) <= LDS,
+                  "LDS layout");
 
     // Store the chunk v (16 bytes, columns n ..) of a row on the right edge:
     // whole if it lies inside C, else element by element.

@@ -59,16 +59,27 @@ constexpr TileShape tile_shape(int tc) {
                         : TileShape{32, 64, 1, 2};
 }
 
-// Chunks per K-contiguous row of a K-tile.  The large tile halves its K-tile
-// at 3-4 stages so that the ring stays inside the LDS budget (the remedy the
-// skill gives for a buffer over the cliff: halve BK).
-constexpr int cpr_k(int tc, int stages) {
-    return (tc == TILE_L || tc == TILE_W) ? (stages <= 2 ? 8 : 4) : tc == TILE_M ? 8 : 16;
+// The 3-stage direct-to-LDS ring of the 256x256 classes is split by
+// operand: three A slots and two B slots of a full-width K-tile, exactly the
+// 160 KiB of LDS.  The A tile is loaded two K-tiles ahead and the B tile one
+// ahead, where three whole slots would need 192 KiB.
+constexpr bool split_ring(int tc, int stages, int variant) {
+    return variant == VAR_DIRECT && stages == 3 && (tc == TILE_L || tc == TILE_W);
 }
-constexpr int block_k(int dt, int tc, int stages) { return cpr_k(tc, stages) * epc(dt); }
+
+// Chunks per K-contiguous row of a K-tile.  The large tile halves its K-tile
+// where the ring would not fit the LDS budget otherwise (the remedy the
+// skill gives for a buffer over the cliff: halve BK): at 4 stages, and at 3
+// stages for the register-staged variant.
+constexpr int cpr_k(int tc, int stages, int variant) {
+    return (tc == TILE_L || tc == TILE_W) ? ((stages <= 2 || split_ring(tc, stages, variant)) ? 8 : 4)
+         : tc == TILE_M ? 8 : 16;
+}
+constexpr int block_k(int dt, int tc, int stages, int variant) { return cpr_k(tc, stages, variant) * epc(dt); }
 
 // LDS slots of the ring and register staging sets per variant:
-//  direct-to-LDS: `stages` slots, stages-1 tiles in flight, no staging set;
+//  direct-to-LDS: `stages` slots, stages-1 tiles in flight, no staging set
+//  (split ring: three A slots, two B slots);
 //  register-staged: min(stages, 2) slots and max(1, stages-1) staging sets,
 //  each holding one tile in flight.
 constexpr int lds_slots(int variant, int stages) {
@@ -81,12 +92,14 @@ constexpr int tiles_in_flight(int variant, int stages) {
     return variant == VAR_DIRECT ? stages - 1 : reg_sets(variant, stages);
 }
 
-// Bytes of one ring slot (A tile followed by B tile).
-constexpr int slot_bytes(int dt, int tc, int stages) {
-    return (tile_shape(tc).bm + tile_shape(tc).bn) * block_k(dt, tc, stages) * in_size(dt);
+// Bytes of one ring slot (A tile followed by B tile), and of the ring.
+constexpr int slot_bytes(int dt, int tc, int stages, int variant) {
+    return (tile_shape(tc).bm + tile_shape(tc).bn) * block_k(dt, tc, stages, variant) * in_size(dt);
 }
 constexpr int ring_bytes(int dt, int tc, int stages, int variant) {
-    return slot_bytes(dt, tc, stages) * lds_slots(variant, stages);
+    return split_ring(tc, stages, variant)
+               ? (3 * tile_shape(tc).bm + 2 * tile_shape(tc).bn) * block_k(dt, tc, stages, variant) * in_size(dt)
+               : slot_bytes(dt, tc, stages, variant) * lds_slots(variant, stages);
 }
 // The epilogue reuses LDS to stage one 32-row strip of C per wave; a strip
 // row is the wave's block width plus padding that spreads the rows over the
@@ -106,11 +119,11 @@ constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
 constexpr int threads(int tc) { return tile_shape(tc).wm * tile_shape(tc).wn * 64; }
 
 // 16-byte loads per lane per K-tile for each operand.
-constexpr int loads_a(int dt, int tc, int stages) {
-    return tile_shape(tc).bm * (block_k(dt, tc, stages) * in_size(dt) / kChunk) / threads(tc);
+constexpr int loads_a(int dt, int tc, int stages, int variant) {
+    return tile_shape(tc).bm * (block_k(dt, tc, stages, variant) * in_size(dt) / kChunk) / threads(tc);
 }
-constexpr int loads_b(int dt, int tc, int stages) {
-    return tile_shape(tc).bn * (block_k(dt, tc, stages) * in_size(dt) / kChunk) / threads(tc);
+constexpr int loads_b(int dt, int tc, int stages, int variant) {
+    return tile_shape(tc).bn * (block_k(dt, tc, stages, variant) * in_size(dt) / kChunk) / threads(tc);
 }
 
 // XOR swizzle of a K-contiguous row (see the header comment).  It depends
@@ -167,9 +180,9 @@ constexpr int k_phys_tile(int t, int head, int nbody, int rot) {
 constexpr bool instance_fits(int dt, int tc, int stages, int variant) {
     return stages >= 1 && stages <= kMaxStages
         && lds_bytes(dt, tc, stages, variant) <= kLdsBudget
-        && (tile_shape(tc).bm * cpr_k(tc, stages)) % threads(tc) == 0
-        && (tile_shape(tc).bn * cpr_k(tc, stages)) % threads(tc) == 0
-        && loads_a(dt, tc, stages) >= 1 && loads_b(dt, tc, stages) >= 1;
+        && (tile_shape(tc).bm * cpr_k(tc, stages, variant)) % threads(tc) == 0
+        && (tile_shape(tc).bn * cpr_k(tc, stages, variant)) % threads(tc) == 0
+        && loads_a(dt, tc, stages, variant) >= 1 && loads_b(dt, tc, stages, variant) >= 1;
 }
 
 }  // namespace pg

@@ -62,6 +62,21 @@ int main() {
             for (int s = 1; s <= kMaxStages; ++s)
                 for (int v = 0; v < 2; ++v)
                     if (!instance_fits(dt, tc, s, v)) { std::printf("over budget %d %d %d %d\n", dt, tc, s, v); ++fail; }
+    // The split ring (3 direct stages at 256x256): three A slots and two B
+    // slots of the full K-tile fill the 160 KiB exactly; the register-staged
+    // 3-stage instances of the same class halve the K-tile instead.
+    for (int dt = 0; dt < 4; ++dt)
+        for (int tc = 0; tc < TILE_COUNT; ++tc) {
+            const bool big = tc == TILE_L || tc == TILE_W;
+            if (split_ring(tc, 3, VAR_DIRECT) != big || split_ring(tc, 3, VAR_REG) || split_ring(tc, 2, VAR_DIRECT) ||
+                split_ring(tc, 4, VAR_DIRECT)) ++fail;
+            if (big && (block_k(dt, tc, 3, VAR_DIRECT) != block_k(dt, tc, 2, VAR_DIRECT) ||
+                        2 * block_k(dt, tc, 3, VAR_REG) != block_k(dt, tc, 2, VAR_REG) ||
+                        ring_bytes(dt, tc, 3, VAR_DIRECT) != kLdsBudget)) {
+                std::printf("split ring %d %d\n", dt, tc);
+                ++fail;
+            }
+        }
     // Layout RR: the transposing fragment reads of the N-contiguous B tile
     // (lane addresses exactly as the kernel forms them) hit 64 different
     // 4-byte banks in every group of 32 lanes, and the XOR keeps each row a
@@ -110,13 +125,14 @@ int main() {
     // halves at 3-4 stages -- the same sequence of MFMA k-slices (2 chunks
     // each) at both K-tile sizes, so all stage counts sum in one order.
     int order_fail = 0;
+    for (int v = 0; v < 2; ++v)
     for (int dt = 0; dt < 4; ++dt)
         for (int tc = 0; tc < TILE_COUNT; ++tc) {
-            const int bkmax = block_k(dt, tc, 1), slice = 2 * epc(dt);
+            const int bkmax = block_k(dt, tc, 1, v), slice = 2 * epc(dt);
             for (int K = 1; K <= 9 * bkmax; K += (K < 3 * bkmax ? 1 : 7)) {
                 int seq[2][1024], len[2] = {0, 0};
                 for (int s = 1; s <= kMaxStages; ++s) {
-                    const int bk = block_k(dt, tc, s), nt = (K + bk - 1) / bk;
+                    const int bk = block_k(dt, tc, s, v), nt = (K + bk - 1) / bk;
                     const int head = k_head_tiles(K, bk, bkmax), nbody = nt - head;
                     if (head > (s == 1 ? 1 : s - 1)) ++order_fail;   // head tiles are prologue loads
                     for (int rot = 0; rot < (nbody > 0 ? nbody : 1); rot += 1 + nbody / 5) {
@@ -152,15 +168,16 @@ int main() {
     // Every (P, rot_u): the splits together cover each physical tile once,
     // and the 1-stage and 3-stage K-tiles add the same k-slices in one order.
     int split_fail = 0;
+    for (int v = 0; v < 2; ++v)
     for (int dt = 0; dt < 4; ++dt)
         for (int tc = 0; tc < TILE_COUNT; ++tc) {
-            const int bkmax = block_k(dt, tc, 1), slice = 2 * epc(dt);
+            const int bkmax = block_k(dt, tc, 1, v), slice = 2 * epc(dt);
             for (int K = 1; K <= 9 * bkmax; K += (K < 3 * bkmax ? 5 : 11))
                 for (int P = 1; P <= 3; ++P)
                     for (int rot_u = 0; rot_u < 9; rot_u += 4) {
                         int seq[2][1024], len[2] = {0, 0};
                         for (int si = 0; si < 2; ++si) {
-                            const int s = si == 0 ? 1 : 3, bk = block_k(dt, tc, s), per = bkmax / bk;
+                            const int s = si == 0 ? 1 : 3, bk = block_k(dt, tc, s, v), per = bkmax / bk;
                             const int nt = (K + bk - 1) / bk, units = K / bkmax, head = k_head_tiles(K, bk, bkmax);
                             bool seen[2048] = {false};
                             int covered = 0;

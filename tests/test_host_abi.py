@@ -96,17 +96,21 @@ def test_empty_sizes_are_valid():
 
 @pytest.mark.parametrize("dtype,bk2,bk4", [("bf16", 64, 32), ("f16", 64, 32), ("i8", 128, 64), ("f32", 32, 16)])
 def test_large_tile_budget(dtype, bk2, bk4):
-    """256x256 tiles: the K-tile halves at 3-4 stages so the ring fits 160 KiB."""
+    """256x256 tiles: the K-tile halves where the ring would not fit 160 KiB
+    (4 stages, and 3 register-staged stages); the 3-stage direct ring keeps
+    it and splits by operand: three A slots and two B slots, 160 KiB."""
     sz = {"bf16": 2, "f16": 2, "i8": 1, "f32": 4}[dtype]
     for stages in (1, 2, 3, 4):
         for variant in ("reg", "direct"):
             rc, info = q(dtype=dtype, stages=stages, variant=variant, tile="256x256")
             assert rc == binding.GEMM_OK
-            bk = bk2 if stages <= 2 else bk4
+            split = stages == 3 and variant == "direct"
+            bk = bk2 if stages <= 2 or split else bk4
             assert info["block_k"] == bk
             slots = stages if variant == "direct" else min(stages, 2)
             assert info["lds_slots"] == slots
-            ring = slots * (256 + 256) * bk * sz
+            ring = (3 * 256 + 2 * 256) * bk * sz if split else slots * (256 + 256) * bk * sz
+            assert not split or ring == 160 * 1024
             # the epilogue stages 32 rows of each wave's 128-column block of C
             # (4-byte outputs for int8/fp32, rows padded by 16 B; 2-byte for
             # fp16/bf16, rows padded by 32 B)

@@ -66,6 +66,36 @@ def direct_program(S, nt, fault=None):
     return ev
 
 
+def split_program(nt, fault=None):
+    """The 3-stage direct ring of the 256x256 tiles, split by operand: A
+    slots ("A", t % 3), B slots ("B", t % 2).  Loads carry LA = LB = HALF
+    chunks each.  While tile kt is multiplied the A tile of kt+2 is loaded;
+    after the barrier that ends tile kt, the B tile of kt+2."""
+    ev = []
+    for t in range(2):                                      # prologue: tiles 0 and 1
+        ev.append(("load", t, ("A", t % 3), 0, HALF))
+        ev.append(("load", t, ("B", t % 2), HALF, LPT))
+    ev.append(("wait", LPT))
+    ev.append(("barrier",))
+    ev.append(("read", ("A", 0), 0))
+    ev.append(("read", ("B", 0), 0))
+    for kt in range(nt):
+        ev.append(("read", ("A", kt % 3), kt))              # steps 1..KSTEPS-1
+        ev.append(("read", ("B", kt % 2), kt))
+        a_slot = (kt + 1) % 3 if fault == "slot" else (kt + 2) % 3
+        ev.append(("load", kt + 2, ("A", a_slot), 0, HALF))
+        ev.append(("wait", LPT if fault == "wait" else HALF))
+        if fault != "barrier":
+            ev.append(("barrier",))
+        ev.append(("read", ("A", (kt + 1) % 3), kt + 1))    # next tile's step 0
+        ev.append(("read", ("B", (kt + 1) % 2), kt + 1))
+        b_slot = (kt + 1) % 2 if fault == "bslot" else kt % 2
+        ev.append(("load", kt + 2, ("B", b_slot), HALF, LPT))
+    if fault != "drain":
+        ev.append(("wait", 0))
+    return ev
+
+
 def reg_program(S, nt, fault=None):
     ev = []
     if S == 1:
@@ -164,15 +194,16 @@ def check(events, nt, S):
         done = [w for w in writes if w[1] < e and (w[2] is None or (w[2][4] is not None and w[2][4] < e))]
         racing = [w for w in writes if w[1] <= e and w not in done]
         if racing:
-            raise Violation("read of slot %d (tile %d) in epoch %d races with a write of tile %d"
+            raise Violation("read of slot %s (tile %d) in epoch %d races with a write of tile %d"
                             % (slot, tile, e, racing[0][0]))
         # the last landed write must be this tile (both halves for LDS-DMA)
         last = [w for w in done if w[0] == done[-1][0]] if done else []
         if not done or done[-1][0] != tile:
-            raise Violation("read of slot %d in epoch %d sees tile %s, wants %d"
+            raise Violation("read of slot %s in epoch %d sees tile %s, wants %d"
                             % (slot, e, done[-1][0] if done else None, tile))
-        if last and last[0][2] is not None and sum(w[2][2] for w in last) != LPT:
-            raise Violation("tile %d only partly in slot %d" % (tile, slot))
+        need = HALF if isinstance(slot, tuple) else LPT      # one operand's chunks, or both
+        if last and last[0][2] is not None and sum(w[2][2] for w in last) != need:
+            raise Violation("tile %d only partly in slot %s" % (tile, slot))
     if seen != set(range(nt)):
         raise Violation("tiles never multiplied: %s" % sorted(set(range(nt)) - seen))
     # no LDS-DMA load -- including the all-zero ones past the last tile --
@@ -211,3 +242,20 @@ def test_planted_schedule_mistakes_are_caught(variant, S, fault):
 def test_missing_drain_wait_is_caught():
     with pytest.raises(Violation):
         check(direct_program(3, 1, "drain"), 1, 3)
+
+
+def test_split_ring_is_race_free():
+    for nt in range(1, 13):
+        check(split_program(nt), nt, 3)
+
+
+@pytest.mark.parametrize("fault", ["slot", "bslot", "wait", "barrier", "drain"])
+def test_split_ring_mistakes_are_caught(fault):
+    caught = False
+    for nt in range(1, 13):
+        try:
+            check(split_program(nt, fault), nt, 3)
+        except Violation:
+            caught = True
+            break
+    assert caught, fault
