@@ -22,12 +22,12 @@ WORKLOADS = {
     "fp16_4096_rc": (4096, 4096, 4096, "f16", "RC", "normal", 1.0 / 64.0, ALL_PAIRS),
     "bf16_skinny_8192x64x8192": (8192, 64, 8192, "bf16", "RC", "normal", 1.0, ALL_PAIRS),
     "bf16_8192x8192x8200": (8192, 8192, 8200, "bf16", "RC", "uniform", 1.0,
-                            [(4, "direct"), (4, "reg"), (2, "direct"), (1, "direct")]),
+                            [(3, "direct"), (4, "direct"), (4, "reg"), (2, "direct"), (1, "direct")]),
     # layout RR at the 256x256 tile (B fragments by transposing LDS reads)
     "fp16_4096_rr": (4096, 4096, 4096, "f16", "RR", "normal", 1.0 / 64.0,
-                     [(2, "direct"), (2, "reg"), (4, "direct"), (1, "direct"), (3, "reg")]),
+                     [(3, "direct"), (2, "direct"), (2, "reg"), (4, "direct"), (1, "direct"), (3, "reg")]),
     "int8_4096_rr": (4096, 4096, 4096, "i8", "RR", "int", 1.0,
-                     [(2, "direct"), (2, "reg"), (4, "direct"), (1, "reg")]),
+                     [(3, "direct"), (2, "direct"), (2, "reg"), (4, "direct"), (1, "reg")]),
 }
 
 
@@ -109,7 +109,7 @@ def test_tile_loop_with_edges(name, tile):
                                   rows, cols)
         ad, bd = a.cuda(), b.cuda()
         first = None
-        for stages, variant in [(2, "direct"), (1, "direct"), (3, "reg"), (4, "direct")]:
+        for stages, variant in [(2, "direct"), (3, "direct"), (1, "direct"), (3, "reg"), (4, "direct")]:
             print("  stages=%d variant=%s" % (stages, variant), flush=True)
             c = alloc_c(M, N, N, dtype)
             binding.gemm_run(gg.h, M, N, K, dtype, "RC", stages, variant, ad, K, bd, K, c, N)
