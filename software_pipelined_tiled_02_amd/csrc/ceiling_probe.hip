@@ -18,8 +18,9 @@
 // cycles the matrix cores are busy (rate / (per-clock datasheet rate x clock)).
 //
 // HBM ceiling.  A 1 GiB buffer (four times the Infinity Cache) read once with
-// 16-byte loads, each workgroup sweeping one contiguous block; and the same
-// buffer copied to a second one.
+// 16-byte loads, each workgroup sweeping one contiguous block; the same
+// buffer copied to a second one; and 1 GiB written with the 16-byte
+// non-temporal stores the GEMM writes C with.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -168,6 +169,19 @@ __global__ void __launch_bounds__(256) hbm_copy(const i32x4* __restrict__ src, i
     }
 }
 
+// Each workgroup writes one contiguous block with 16-byte non-temporal
+// stores, the store the GEMM's epilogue uses for C.
+__global__ void __launch_bounds__(256) hbm_write(i32x4* __restrict__ dst, uint64_t per_wg) {
+    const uint64_t base = (uint64_t)blockIdx.x * (per_wg / 16);
+    const i32x4 v = {(int)blockIdx.x, (int)threadIdx.x, 1, 2};
+    for (uint64_t u = threadIdx.x; u < per_wg / 16; u += 4 * 256) {
+        __builtin_nontemporal_store(v, dst + base + u);
+        __builtin_nontemporal_store(v, dst + base + u + 256);
+        __builtin_nontemporal_store(v, dst + base + u + 512);
+        __builtin_nontemporal_store(v, dst + base + u + 768);
+    }
+}
+
 #define CHECK(x)                                                                 \
     do {                                                                         \
         hipError_t e_ = (x);                                                     \
@@ -259,6 +273,13 @@ int main() {
     CHECK(hipEventSynchronize(e1));
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     std::printf("hbm_copy: %.1f GB/s (read + write bytes, 1 GiB each way)\n", 2.0 * bytes * 10 / (ms * 1e-3) / 1e9);
+    for (int w = 0; w < 3; ++w) hipLaunchKernelGGL(hbm_write, dim3(wgs), dim3(256), 0, 0, dst, per_wg);
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < 10; ++r) hipLaunchKernelGGL(hbm_write, dim3(wgs), dim3(256), 0, 0, dst, per_wg);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("hbm_write: %.1f GB/s (1 GiB, 16-byte non-temporal stores)\n", (double)bytes * 10 / (ms * 1e-3) / 1e9);
     CHECK(hipFree(src));
     CHECK(hipFree(dst));
     CHECK(hipFree(out));
