@@ -282,7 +282,12 @@ int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype,
     e = hipLaunchKernel(fn, dim3((unsigned)plan.info.grid), dim3((unsigned)plan.info.threads), kargs, 0,
                         (hipStream_t)stream);
     if (e == hipSuccess) e = hipGetLastError();
-    if (cur != h->device) hipSetDevice(cur);
+    if (cur != h->device) {
+        // put the caller's device back; a failure here is reported unless
+        // the launch itself already failed
+        const hipError_t r = hipSetDevice(cur);
+        if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return hip_fail(e);
     return GEMM_OK;
 }

@@ -430,7 +430,6 @@ struct Gemm {
                                                     int st, int r, Frags& f) {
         const uint8_t PG_LDS* as = smem + a_off(slot);
         const uint8_t PG_LDS* bs = smem + b_off(slot);
-        const int lane = s.tid & 63;
         if (r < FM) {
             f.y[r] = *(const i32x4 PG_LDS*)(as + (s.wm * WTM + r * 32) * CPR * kChunk + s.rd[st]);
         } else {
