@@ -40,6 +40,20 @@ def draw(rng):
 
 
 CASES = [draw(random.Random(1000 + i)) for i in range(48)]
+# The 3-stage direct ring of the 256x256 tiles (split by operand): more
+# cases of it than the draw above gives, with every other option random and
+# K long enough for the ring to wrap several times.
+SPLIT_RING = []
+for i in range(16):
+    rng = random.Random(5000 + i)
+    case = draw(rng)
+    e = EPC[case["dtype"]]
+    K = max(e, rng.randint(300, 4000) // e * e)
+    case.update(variant="direct", stages=3, tile=rng.choice(("256x256", "256x256w8")), K=K,
+                pad=e * rng.randint(0, 2), off=0, M=rng.randint(200, 700), N=case["N"] if case["layout"] == "RR"
+                else rng.randint(200, 600))
+    SPLIT_RING.append(case)
+CASES += SPLIT_RING
 
 
 @pytest.fixture(scope="module")
