@@ -16,6 +16,8 @@
 // depends on the operand bits; the effective clock is reported from
 // s_memtime against the fixed 100 MHz s_memrealtime, and with it the share of
 // cycles the matrix cores are busy (rate / (per-clock datasheet rate x clock)).
+// A third figure (prefix mfma16_) runs the LDS-fed loop with 16x16 MFMA
+// blocks, which the GEMM does not use.
 //
 // HBM ceiling.  A 1 GiB buffer (four times the Infinity Cache) read once with
 // 16-byte loads, each workgroup sweeping one contiguous block; the same
@@ -146,6 +148,74 @@ __global__ void __launch_bounds__(256) mfma_ceiling(int iters, int* out, unsigne
     }
 }
 
+// The same loop with 16x16 MFMA blocks (16x16x32 for fp16/bf16, 16x16x64 for
+// int8): 8 x 8 blocks per wave cover the same 128 x 128 accumulator tile, and
+// each k-step reads 16 fragments for 64 MFMAs -- the same LDS bytes per
+// multiply-add as the 32x32 loop.  Operands from LDS, read one step ahead.
+template <int DT>
+__device__ __forceinline__ i32x4 mma16(i32x4 x, i32x4 y, i32x4 c) {
+    if constexpr (DT == I8) {
+        return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, c, 0, 0, 0);
+    } else if constexpr (DT == BF16) {
+        return __builtin_bit_cast(i32x4, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), __builtin_bit_cast(f32x4, c), 0, 0, 0));
+    } else {
+        return __builtin_bit_cast(i32x4, __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), __builtin_bit_cast(f32x4, c), 0, 0, 0));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void probe_step16(i32x4 (&acc)[8][8], const i32x4 (&x)[8], const i32x4 (&y)[8],
+                                             i32x4 (&nx)[8], i32x4 (&ny)[8], const i32x4 LDSP* lds, int next,
+                                             int lane) {
+#pragma unroll
+    for (int u = 0; u < 64; ++u) {
+        acc[u / 8][u % 8] = mma16<DT>(x[u % 8], y[u / 8], acc[u / 8][u % 8]);
+        if (u % 4 == 0) {
+            // unit index < 64 * 64 = kLdsUnits
+            const int r = u / 4;
+            if (r < 8) nx[r] = lds[((next * 16 + r) & 63) * 64 + lane];
+            else ny[r - 8] = lds[((next * 16 + r) & 63) * 64 + lane];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) mfma16_ceiling(int iters, int* out, unsigned long long* clk) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kLdsUnits * 16];
+    i32x4 LDSP* lds = (i32x4 LDSP*)lds_raw;
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < kLdsUnits; i += 256) lds[i] = random_unit(DT, (uint32_t)i, blockIdx.x);
+    __syncthreads();
+    i32x4 acc[8][8];
+    for (int a = 0; a < 8; ++a)
+        for (int b = 0; b < 8; ++b) acc[a][b] = i32x4{0, 0, 0, 0};
+    i32x4 x0[8], y0[8], x1[8], y1[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        x0[a] = lds[a * 64 + lane];
+        y0[a] = lds[(8 + a) * 64 + lane];
+        x1[a] = lds[(16 + a) * 64 + lane];
+        y1[a] = lds[(24 + a) * 64 + lane];
+    }
+    const unsigned long long t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; it += 2) {   // iters is even
+        probe_step16<DT>(acc, x0, y0, x1, y1, lds, it + 1, lane);
+        probe_step16<DT>(acc, x1, y1, x0, y0, lds, it + 2, lane);
+    }
+    const unsigned long long t1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
+    int s = 0;
+    for (int a = 0; a < 8; ++a)
+        for (int b = 0; b < 8; ++b) s ^= acc[a][b][0] ^ acc[a][b][3];
+    out[blockIdx.x * 256 + tid] = s;
+    if (tid == 0) {
+        clk[blockIdx.x * 2] = t1 - t0;
+        clk[blockIdx.x * 2 + 1] = r1 - r0;
+    }
+}
+
 // Each workgroup reads (and for the copy, writes) one contiguous block of
 // `per_wg` bytes, 4 x 16 bytes per lane per pass.
 __global__ void __launch_bounds__(256) hbm_read(const i32x4* __restrict__ src, uint64_t per_wg, int* out) {
@@ -232,6 +302,45 @@ int run_mfma(const char* name, double peak, int cus) {
     return 0;
 }
 
+template <int DT>
+int run_mfma16(const char* name, double peak, int cus) {
+    int* out;
+    unsigned long long* clk;
+    CHECK(hipMalloc(&out, (size_t)cus * 256 * sizeof(int)));
+    CHECK(hipMalloc(&clk, (size_t)cus * 2 * sizeof(unsigned long long)));
+    const int iters = 4000;   // one iteration: k = 32 (int8: 64) over the 128 x 128 tile
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    for (int w = 0; w < 3; ++w) mfma16_ceiling<DT><<<dim3(cus), dim3(256)>>>(iters, out, clk);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    const int reps = 5;
+    for (int r = 0; r < reps; ++r) mfma16_ceiling<DT><<<dim3(cus), dim3(256)>>>(iters, out, clk);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    ms /= reps;
+    std::vector<unsigned long long> h((size_t)cus * 2);
+    CHECK(hipMemcpy(h.data(), clk, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+    double cyc = 0, rt = 0;
+    for (int b = 0; b < cus; ++b) {
+        cyc += (double)h[2 * b];
+        rt += (double)h[2 * b + 1];
+    }
+    const double ghz = cyc / (rt / 100e6) / 1e9;
+    const double ops = 2.0 * 64 * 16 * 16 * (DT == I8 ? 64 : 32) * 4 * (double)cus * iters;
+    const double t = ops / (ms * 1e-3) / 1e12;
+    const double busy = t / (peak * ghz / 2.4);
+    std::printf("mfma16_%s: %.1f %s, effective clock %.3f GHz, %.1f%% of the %.1f datasheet peak, "
+                "matrix cores busy %.1f%% of cycles\n", name, t, DT == I8 ? "TOP/s" : "TFLOP/s", ghz,
+                100.0 * t / peak, peak, 100.0 * busy);
+    CHECK(hipFree(out));
+    CHECK(hipFree(clk));
+    return 0;
+}
+
 }  // namespace
 
 int main() {
@@ -241,6 +350,9 @@ int main() {
     std::printf("compute_units: %d\n", cus);
     if (run_mfma<I8, true>("int8", 5033.2, cus) || run_mfma<F16, true>("fp16", 2516.6, cus) ||
         run_mfma<BF16, true>("bf16", 2516.6, cus) || run_mfma<F32, true>("fp32", 157.3, cus))
+        return 1;
+    if (run_mfma16<I8>("int8", 5033.2, cus) || run_mfma16<F16>("fp16", 2516.6, cus) ||
+        run_mfma16<BF16>("bf16", 2516.6, cus))
         return 1;
     if (run_mfma<I8, false>("int8", 5033.2, cus) || run_mfma<F16, false>("fp16", 2516.6, cus) ||
         run_mfma<BF16, false>("bf16", 2516.6, cus))
