@@ -104,14 +104,15 @@ def read_traffic(workload, stages, variant):
     return float(vals[key]) if key in vals else None
 
 
-def measured_ceiling(dtype, bound):
-    """The chip's attainable rate for this dtype (MFMA loop fed from LDS with
-    random data) or for HBM (streaming read), from the committed output of
-    ceiling_probe; None if absent."""
+def measured_ceiling(dtype, bound, block=32):
+    """The chip's attainable rate for this dtype (MFMA loop of the kernel's
+    block shape, fed from LDS with random data) or for HBM (streaming read),
+    from the committed output of ceiling_probe; None if absent."""
     path = os.path.join(ROOT, "profiles", "ceilings.txt")
     if not os.path.exists(path):
         return None
-    key = "hbm_read" if bound == "hbm" else "mfma_" + {"i8": "int8", "f16": "fp16", "bf16": "bf16", "f32": "fp32"}[dtype]
+    prefix = "mfma16_" if block == 16 else "mfma_"
+    key = "hbm_read" if bound == "hbm" else prefix + {"i8": "int8", "f16": "fp16", "bf16": "bf16", "f32": "fp32"}[dtype]
     for line in open(path):
         if line.startswith(key + ":"):
             return float(line.split(":", 1)[1].split()[0])
@@ -300,11 +301,12 @@ def main():
         roof = {"bound": "mfma", "achieved": round(r["tops"], 1), "peak": PEAK[dtype], "unit": unit,
                 "frac": round(r["tops"] / PEAK[dtype], 4)}
     roof["traffic"] = read_traffic(args.workload, best[0], best[1])
-    ceil = measured_ceiling(dtype, bound)
+    ceil = measured_ceiling(dtype, bound, info["mfma_block"])
     if ceil:
         roof["measured_ceiling"] = {"value": ceil, "unit": roof["unit"], "frac": round(roof["achieved"] / ceil, 4),
-                                    "source": "profiles/ceilings.txt (ceiling_probe: MFMA fed from LDS with "
-                                              "random data / HBM streaming read)"}
+                                    "source": "profiles/ceilings.txt (ceiling_probe: %s fed from LDS with random "
+                                              "data / HBM streaming read)" % (
+                                                  "%dx%d MFMA blocks" % (info["mfma_block"], info["mfma_block"]))}
     hot = None
     if bound == "hbm":
         # The same buffers every launch: A fits in the Infinity Cache, so this
@@ -333,7 +335,8 @@ def main():
         "config": {"workload": desc, "M": M, "N": N, "K": K, "layout": layout,
                    "stages": best[0], "variant": best[1],
                    "tile": "%dx%dx%d" % (info["block_m"], info["block_n"], info["block_k"]),
-                   "lds_bytes": info["lds_bytes"], "grid": info["grid"], "splits": info["splits"]},
+                   "lds_bytes": info["lds_bytes"], "grid": info["grid"], "splits": info["splits"],
+                   "mfma_block": info["mfma_block"]},
         "roofline": roof,
         "pairs_bit_identical": identical,
         "rounds": args.rounds,

@@ -42,7 +42,7 @@ class ConfigInfo(ctypes.Structure):
         "tile", "block_m", "block_n", "block_k", "waves_m", "waves_n", "threads", "lds_slots",
         "reg_sets", "tiles_in_flight", "lds_bytes", "loads_per_tile")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
-        ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("mfma_block", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):

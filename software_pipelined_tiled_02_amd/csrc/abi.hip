@@ -126,6 +126,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.tiles_in_flight = pg::tiles_in_flight(variant, stages);
     in.lds_bytes = pg::lds_bytes(dtype, tc, stages, variant);
     in.loads_per_tile = pg::loads_a(dtype, tc, stages, variant) + pg::loads_b(dtype, tc, stages, variant);
+    in.mfma_block = pg::mfma_block16(dtype, layout, tc, stages, variant) ? 16 : 32;
     // The 256x256 tiles run one workgroup per CU (their LDS ring and
     // registers allow no second one); with more tiles than CUs, a grid of
     // one workgroup per CU loops over the tiles, so that one tile's C stores

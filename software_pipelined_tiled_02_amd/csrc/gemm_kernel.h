@@ -29,7 +29,8 @@
 //
 // MFMA mapping.  Both operands are read from LDS as one 16-byte chunk per
 // lane: lane l takes row (l % 32) of a 32-row fragment and chunk
-// (2*step + l/32) of the K-tile.  The B-side fragment is fed as the MFMA's
+// (2*step + l/32) of the K-tile.  (The 256x256 instances of the 2-3 stage
+// direct ring with K-contiguous B use 16x16 blocks instead; see Block16.)  The B-side fragment is fed as the MFMA's
 // first operand and the A-side fragment as its second, so the 32x32 result
 // block is C^T and each lane ends up holding four consecutive columns of
 // one row of C -- which the epilogue stores as one vector per lane.
@@ -58,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernel_args.h"
 #include "tile_layout.h"
 
@@ -83,6 +86,31 @@ constexpr int kScopeDevice = 16;
 
 template <int DT> struct AccT { typedef f32x16 type; };
 template <> struct AccT<DT_I8> { typedef i32x16 type; };
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16x16 MFMA block step: acc += X * Y over 4 chunks of k (one 16-byte
+// chunk per lane of each operand: 32 k for fp16/bf16, 64 for int8).  The
+// matrix cores hold a 0.25-0.3 GHz higher clock on these than on the 32x32
+// blocks at the same busy share (measured), and the results are the same
+// bits.  Written in place (accumulator tied to the destination): with the
+// compiler's own form, the 64 accumulator blocks of a wave moved between
+// registers at every K-tile.  The compiler does not see these as MFMAs, so
+// the loop that issues them pads the hazards around it itself (Block16).
+//   The accumulator is held as four 32-bit words of either type (fp32 bits
+// for fp16/bf16): typed as float vectors, the compiler kept them in arch
+// VGPRs around the statements that tie them (below) and spilled.
+template <int DT>
+__device__ __forceinline__ i32x4 mfma16(i32x4 x, i32x4 y, i32x4 c) {
+    if constexpr (DT == DT_BF16) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    } else if constexpr (DT == DT_F16) {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    } else {
+        static_assert(DT == DT_I8, "16x16 blocks: int8, fp16, bf16");
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
+    }
+    return c;
+}
 
 // One 32x32 MFMA block step: acc += X * Y over the k values held in one
 // 16-byte chunk per lane of each operand.
@@ -137,8 +165,13 @@ struct Gemm {
     static constexpr int CPR = cpr_k(TC, STAGES, VARIANT); // chunks per K-contiguous row
     static constexpr int BK = CPR * EPC;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KSTEPS = CPR / 2;                  // two chunks per MFMA step
+    // 16x16 MFMA blocks (see mfma_block16: the 4-wave 256x256 tile's 2-3
+    // stage direct rings with K-contiguous B, which carry the large square
+    // shapes; two 16x16 steps per K-tile); 32x32 blocks everywhere else.
+    static constexpr bool B16 = mfma_block16(DT, LAYOUT, TC, STAGES, VARIANT);
+    static constexpr int BS = B16 ? 16 : 32;                // MFMA block edge
+    static constexpr int FM = WTM / BS, FN = WTN / BS;
+    static constexpr int KSTEPS = CPR / (B16 ? 4 : 2);      // chunks per MFMA step: 2 (32x32) or 4 (16x16)
     static constexpr int LA = loads_a(DT, TC, STAGES, VARIANT), LB = loads_b(DT, TC, STAGES, VARIANT);
     static constexpr int LPT = LA + LB;
     static constexpr int A_BYTES = BM * CPR * kChunk;
@@ -151,7 +184,7 @@ struct Gemm {
     static constexpr bool SPLIT = split_ring(TC, STAGES, VARIANT);   // three A slots, two B slots
     static constexpr int CPR_BRR = BN * SZ / kChunk;       // chunks per row of a K x N B tile
     static constexpr int RB_RR = BN * SZ;                   // bytes per row of a K x N B tile
-    typedef typename AccT<DT>::type acc_t;
+    typedef typename std::conditional<B16, i32x4, typename AccT<DT>::type>::type acc_t;
 
     static_assert(instance_fits(DT, TC, STAGES, VARIANT), "instance over budget");
     static_assert(FM >= 1 && FN >= 1, "wave tile");
@@ -159,6 +192,7 @@ struct Gemm {
     static_assert(!RR || (BK * CPR_BRR) % T == 0, "RR loader");
     static_assert(LPT * (STAGES > 1 ? STAGES - 1 : 1) < 64, "vmcnt range");
     static_assert(KSTEPS >= 2, "at least two MFMA steps per K-tile");
+    static_assert(!B16 || (FM == 8 && FN == 8 && KSTEPS == 2), "16x16 blocks: 8 x 8 per wave, two steps");
 
     // ---- per-lane state --------------------------------------------------
     struct State {
@@ -166,6 +200,7 @@ struct Gemm {
         uint32_t offa[LA], offb[LB];   // byte offsets at K-tile 0 (rows past M or N: the tile's row 0)
         uint32_t kca[LA], kcb[LB];     // K index the chunk starts at, inside the tile
         uint32_t rd[KSTEPS];           // per-lane LDS read offset of each MFMA step
+        uint32_t rd16[B16 ? KSTEPS : 1][2];   // 16x16: the same, per 16-row half of a 32-row group
         uint32_t rrb[RR ? FN : 1];     // layout RR: per-lane B fragment read offset (step 0)
         uint32_t kb_step;              // byte advance of the B offset per K-tile
         int K, nt;                     // K; K-tiles this workgroup multiplies
@@ -499,6 +534,85 @@ struct Gemm {
         }
     }
 
+    // ---- 16x16 blocks (B16) -------------------------------------------------
+    //
+    // A wave's 128x128 block is 8 x 8 blocks of 16x16, and a step (4 chunks
+    // of k) needs 8 A-side and 8 B-side fragments -- twice the 32x32 step's.
+    // Double-buffered they would not fit the 256 arch VGPRs, so there is one
+    // fragment set, refilled in quadrant order: a step runs quadrants
+    // (A 0-3 x B 0-3), (A 0-3 x B 4-7), (A 4-7 x B 0-3), (A 4-7 x B 4-7).
+    // It reads its own fragments B 4-7 and A 4-7 during the first quadrant,
+    // the next step's A 0-3 during the third (their last use was the second)
+    // and the next step's B 0-3 during the fourth (last use: the third).
+    // Every read has 4-12 MFMAs between the last use of its registers and
+    // itself, and 12 or more before its first use.
+    //
+    // Fragment idx of a side (0-7: rows 16 idx .. of the wave's block) of
+    // step st of the K-tile in `slot`: lane l takes row (l % 16) and chunk
+    // (4 st + l / 16).
+    __device__ static __forceinline__ void read16(const State& s, const uint8_t PG_LDS* smem, int slot, int st,
+                                                  bool a_side, int idx, Frags& f) {
+        if (a_side)
+            f.y[idx] = *(const i32x4 PG_LDS*)(smem + a_off(slot) + (s.wm * WTM + (idx >> 1) * 32) * CPR * kChunk +
+                                              s.rd16[st][idx & 1]);
+        else
+            f.x[idx] = *(const i32x4 PG_LDS*)(smem + b_off(slot) + (s.wn * WTN + (idx >> 1) * 32) * CPR * kChunk +
+                                              s.rd16[st][idx & 1]);
+    }
+    // One 16x16 step: MFMAs on the fragments of step cst of `cslot` (A/B
+    // 0-3 already in f), reading the rest and the next step's (nslot, nst)
+    // A/B 0-3 as above; loads of chunks [J0, J1) of K-tile ld_kt.  BAR: the
+    // hand-over to the next K-tile -- wait for its data and cross the barrier
+    // after the first quadrant, once this step's own reads of its slot have
+    // completed (the barrier frees the slot for the loads that follow), and
+    // issue the loads after it.
+    template <bool BAR, int WAITN>
+    __device__ static __forceinline__ void step16(const State& s, uint8_t PG_LDS* smem, Frags& f, int cslot,
+                                                  int cst, int nslot, int nst, acc_t (&acc)[FM][FN], int J0,
+                                                  int J1, int ld_kt, int ld_slot, i32x4 (&regs)[LPT]) {
+        const int NL = J1 - J0;
+        constexpr int LU0 = BAR ? 16 : 0;            // loads go in units [LU0, 64)
+        uint32_t ld_sa = 0, ld_sb = 0;
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+            const int q = u / 16, i = u % 16;
+            const int fm = (q >> 1) * 4 + i / 4, fn = (q & 1) * 4 + i % 4;
+            acc[fm][fn] = mfma16<DT>(f.x[fn], f.y[fm], acc[fm][fn]);
+            if (q == 0 && (i & 1) == 0) {
+                const int r = i / 2;                  // B 4-7, then A 4-7
+                read16(s, smem, cslot, cst, r >= 4, 4 + (r & 3), f);
+            }
+            if (q == 2 && (i & 3) == 0) read16(s, smem, nslot, nst, true, i / 4, f);
+            if (q == 3 && i < 4) read16(s, smem, nslot, nst, false, i, f);
+            if (u >= LU0) {
+                if (u == LU0 && NL > 0) {
+                    ld_sa = soff_a(s, ld_kt);
+                    ld_sb = soff_b(s, ld_kt);
+                }
+#pragma unroll
+                for (int j = J0 + (u - LU0) * NL / (64 - LU0); j < J0 + (u - LU0 + 1) * NL / (64 - LU0); ++j)
+                    load_one(s, smem, ld_kt, ld_sa, ld_sb, ld_slot, regs, j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (BAR && u == 15) {
+                wait_vmcnt<WAITN>();
+                block_sync();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // The MFMAs above are inline assembly, so the compiler inserts none of
+    // the wait states around them.  Each K-tile starts with a few (the
+    // accumulators' initial values are ordinary moves made just before the
+    // loop), and the loop is followed by more than any MFMA result needs
+    // before the epilogue reads the accumulators.  (Tying the accumulators
+    // to the padding with empty statements instead made the compiler spill
+    // 53 VGPRs outside the loop.)
+    __device__ static __forceinline__ void mfma16_pad_tile() { asm volatile("s_nop 4" ::: "memory"); }
+    __device__ static __forceinline__ void mfma16_pad_after() {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    }
+
     // Steps 0 .. KSTEPS-2 of the K-tile in `slot`.  On entry f[0] holds step
     // 0's fragments; each step reads the next step's while its MFMAs run (a
     // two-deep register pipeline).  When LOADS, the first LSTEPS steps also
@@ -570,8 +684,20 @@ struct Gemm {
         uint8_t* tp = (uint8_t*)args.ws + kSplitkCounterBytes + (size_t)tile * args.splits * PART;
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(tp, 0, 0x7fffffff, kRsrcWord3);
         // 1. Lane (t, h) holds row t, columns 8q + 4h .. +3 of each 32x32 block
-        //    (per-lane offset in the vector operand, the block's in the scalar one).
-        {
+        //    (per-lane offset in the vector operand, the block's in the scalar
+        //    one); 16x16 blocks likewise.
+        if constexpr (B16) {
+            // 16x16 blocks: lane l holds row (l % 16), columns 4 (l / 16) .. +3
+            const int lane = s.tid & 63;
+            const uint32_t vo = (uint32_t)(((s.wm * WTM + (lane & 15)) * BN + s.wn * WTN + 4 * (lane >> 4)) * 4);
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)p * PART);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    __builtin_amdgcn_raw_buffer_store_b128(acc[fm][fn], rw, vo,
+                                                           so + (uint32_t)((fm * 16 * BN + fn * 16) * 4), kScopeDevice);
+        } else {
             const int lane = s.tid & 63, t = lane & 31, h = lane >> 5;
             const uint32_t vo = (uint32_t)(((s.wm * WTM + t) * BN + s.wn * WTN + 4 * h) * 4);
             const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)p * PART);
@@ -753,7 +879,17 @@ struct Gemm {
 #pragma unroll
         for (int st = 0; st < KSTEPS; ++st) {
             const int t = lane & 31, h = lane >> 5;
-            s.rd[st] = (uint32_t)(t * CPR + ((2 * st + h) ^ swz(CPR, t))) * kChunk;
+            if constexpr (B16) {
+                s.rd[st] = 0;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    // the swizzle depends on the row mod 32; fragments start at multiples of 16
+                    const int row = 16 * half + (lane & 15), c = 4 * st + (lane >> 4);
+                    s.rd16[st][half] = (uint32_t)(row * CPR + (c ^ swz(CPR, row))) * kChunk;
+                }
+            } else {
+                s.rd[st] = (uint32_t)(t * CPR + ((2 * st + h) ^ swz(CPR, t))) * kChunk;
+            }
         }
 
         acc_t acc[FM][FN];
@@ -762,7 +898,7 @@ struct Gemm {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0;
+                for (int v = 0; v < (B16 ? 4 : 16); ++v) acc[fm][fn][v] = 0;
 
         // Every loop below is the K-tile loop restructured into prologue /
         // main loop / drain.  Each K-tile runs steps 0..KSTEPS-2 (tile_body);
@@ -808,9 +944,32 @@ struct Gemm {
             for (int t = 0; t < STAGES - 1; ++t) first_direct(s, smem, t, t);
             wait_vmcnt<(STAGES - 2) * LPT>();
             block_sync();
-            read_first(s, smem, 0, f[0]);
+            if constexpr (B16) {
+                // fragments A/B 0-3 of step 0 (the rest are read in its first quadrant)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    read16(s, smem, 0, 0, true, i, f[0]);
+                    read16(s, smem, 0, 0, false, i, f[0]);
+                }
+            } else {
+                read_first(s, smem, 0, f[0]);
+            }
             if constexpr (!SPLIT) issue_direct<0, HALF>(s, smem, STAGES - 1, STAGES - 1);
             int slot = 0;
+            if constexpr (B16) {
+                // Step 0 carries the loads the body steps carry below; step
+                // 1 is the hand-over.
+                constexpr int BJ0 = SPLIT ? 0 : HALF, BJ1 = SPLIT ? LA : LPT;
+                for (int kt = 0; kt < nt; ++kt) {
+                    const int prev = (slot == 0) ? NSLOT - 1 : slot - 1;
+                    const int next = (slot + 1 == NSLOT) ? 0 : slot + 1;
+                    mfma16_pad_tile();
+                    step16<false, 0>(s, smem, f[0], slot, 0, slot, 1, acc, BJ0, BJ1, kt + STAGES - 1, prev, none);
+                    step16<true, WAITN>(s, smem, f[0], slot, 1, next, 0, acc, HJ0, HJ1, kt + HKT, slot, none);
+                    slot = next;
+                }
+                mfma16_pad_after();
+            } else {
             for (int kt = 0; kt < nt; ++kt) {
                 const int prev = (slot == 0) ? NSLOT - 1 : slot - 1;
                 const int next = (slot + 1 == NSLOT) ? 0 : slot + 1;
@@ -819,6 +978,7 @@ struct Gemm {
                 block_sync();                        // ...all waves; slot of kt free
                 step<true>(s, smem, f[1], f[0], next, 0, acc, HJ0, HJ1, kt + HKT, slot, none);
                 slot = next;
+            }
             }
             wait_vmcnt<0>();   // no LDS write may outlive the loop
         } else {
@@ -881,7 +1041,27 @@ struct Gemm {
         uint8_t PG_LDS* strip = smem + s.wave * STRIP_BYTES;
         const bool full = (mw + WTM <= args.M) && (nw + WTN <= args.N);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
+        for (int fm = 0; fm < (B16 ? FM / 2 : FM); ++fm) {   // 32-row strips
+            if constexpr (B16) {
+                // 16x16 blocks 2 fm and 2 fm + 1: lane l holds row (l % 16),
+                // columns 4 (l / 16) .. +3 of each; the same strip layout
+                // (2-byte outputs: 8-byte halves swapped in rows 8-15, 24-31).
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const int row = 16 * half + (lane & 15), g = lane >> 4;
+                        const acc_t a = acc[2 * fm + half][fn];
+                        if constexpr (OSZ == 4) {
+                            *(i32x4 PG_LDS*)(strip + row * STRIP_ROW + (fn * 16 + 4 * g) * 4) = a;
+                        } else {
+                            const f32x4 af = __builtin_bit_cast(f32x4, a);   // whole vector, then index
+                            const int hs = (g & 1) ^ ((row >> 3) & 1);
+                            *(i32x2 PG_LDS*)(strip + row * STRIP_ROW + (fn * 16 + 8 * (g >> 1)) * 2 + 8 * hs) =
+                                cvt4_16(af[0], af[1], af[2], af[3]);
+                        }
+                    }
+            } else
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll

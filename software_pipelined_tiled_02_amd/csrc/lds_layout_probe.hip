@@ -8,7 +8,12 @@
 // (ds_read_b128 for the K-contiguous fragments of layout RC, the transposing
 // ds_read_b64_tr_b16 for layout RR's N-contiguous B tile) 256 times; the
 // per-lane byte offsets come from a table built on the host exactly as the
-// kernels form them.  Run it under
+// kernels form them.  Patterns rc_* are the read of the 32x32 MFMA blocks
+// (lane l: row l % 32, chunk c0 + l / 32); rc16* that of the 16x16 blocks
+// (lane l: row 16 h + l % 16, chunk c0 + l / 16).  The pair_i_j patterns
+// find which lanes one clock of a 16-byte read serves together: only lanes
+// i and j are active and read the same bank group 256 bytes apart, so the
+// read conflicts exactly when the two lanes share a clock.  Run it under
 //   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS -- ./lds_layout_probe
 // and read the counters dispatch by dispatch in the order it prints.
 #include <hip/hip_runtime.h>
@@ -33,9 +38,10 @@ __global__ void __launch_bounds__(64) probe(const int* __restrict__ offs, int* o
     __shared__ __attribute__((aligned(16))) unsigned char raw[kBytes];
     for (int i = threadIdx.x; i < kBytes / 16; i += 64) ((i32x4 LDSP*)raw)[i] = i32x4{i, i, i, i};
     __syncthreads();
-    const int o = offs[threadIdx.x] & (kBytes - 16);   // keeps every read inside the buffer
+    const int t = offs[threadIdx.x];                    // < 0: the lane takes no part
+    const int o = t & (kBytes - 16);                    // keeps every read inside the buffer
     int acc = 0;
-    for (int r = 0; r < kReps; ++r) {
+    for (int r = 0; r < (t >= 0 ? kReps : 0); ++r) {
         if constexpr (TR) {
             const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDSP*)(raw + (o & ~7)));
             acc += v[0] ^ v[3];
@@ -74,6 +80,34 @@ int main() {
             pats.push_back(p);
         }
     }
+    // The 16x16 blocks' read at chunk c0 = 4 of a 128-byte-row tile, for
+    // both 16-row halves of a 32-row group.  xorprev: the row swizzle the
+    // 128-byte rows had before, (row & 7) ^ ((row >> 3) & 3), conflict-free
+    // for the 32x32 read (also measured here) but not for this one.
+    auto prev8 = [](int row) { return (row & 7) ^ ((row >> 3) & 3); };
+    for (int h = 0; h < 2; ++h) {
+        for (int lay = 0; lay < 4; ++lay) {
+            const char* ln[] = {"_none", "_pad16", "_xor", "_xorprev"};
+            Pattern p{"rc16h" + std::to_string(h) + "_cpr8" + ln[lay], false, {}};
+            for (int l = 0; l < 64; ++l) {
+                const int row = 16 * h + l % 16, chunk = 4 + l / 16, cpr = 8;
+                const int off = lay == 0 ? (row * cpr + chunk) * 16
+                              : lay == 1 ? row * (cpr * 16 + 16) + chunk * 16
+                              : lay == 2 ? phys_chunk(cpr, row, chunk) * 16
+                                         : (row * cpr + (chunk ^ prev8(row))) * 16;
+                p.off.push_back(off);
+            }
+            pats.push_back(p);
+        }
+    }
+    {
+        Pattern p{"rc_cpr8_xorprev", false, {}};
+        for (int l = 0; l < 64; ++l) {
+            const int row = l % 32, chunk = 2 + l / 32;
+            p.off.push_back((row * 8 + (chunk ^ prev8(row))) * 16);
+        }
+        pats.push_back(p);
+    }
     // Layout RR, bf16 B tile of the 256x256 class (512-byte rows): lane j of
     // 16-lane group g addresses 8 bytes of row k at column n (step 1, read 0).
     for (int lay = 0; lay < 3; ++lay) {
@@ -91,11 +125,22 @@ int main() {
         pats.push_back(p);
     }
 
+    // lane pairs: lane i reads byte 0, lane j byte 256 (bank group 0 of the
+    // next 256-byte line), every other lane is off
+    for (int i = 0; i < 64; i += 8)
+        for (int j = 0; j < 64; ++j) {
+            if (j == i) continue;
+            Pattern p{"pair_" + std::to_string(i) + "_" + std::to_string(j), false, std::vector<int>(64, -1)};
+            p.off[i] = 0;
+            p.off[j] = 256;
+            pats.push_back(p);
+        }
+
     int *d_off, *d_out;
     if (hipMalloc(&d_off, 64 * sizeof(int)) != hipSuccess || hipMalloc(&d_out, 64 * sizeof(int)) != hipSuccess) return 1;
     for (size_t i = 0; i < pats.size(); ++i) {
         for (int o : pats[i].off)
-            if (o < 0 || o + 16 > kBytes) { std::printf("offset out of range in %s\n", pats[i].name.c_str()); return 1; }
+            if (o < -1 || o + 16 > kBytes) { std::printf("offset out of range in %s\n", pats[i].name.c_str()); return 1; }
         if (hipMemcpy(d_off, pats[i].off.data(), 64 * sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return 1;
         if (pats[i].tr)
             hipLaunchKernelGGL(probe<1>, dim3(1), dim3(64), 0, 0, d_off, d_out);

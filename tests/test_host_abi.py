@@ -125,6 +125,22 @@ def test_large_tile_budget(dtype, bk2, bk4):
             assert info["tiles_in_flight"] == (stages - 1 if variant == "direct" else max(1, stages - 1))
 
 
+def test_mfma_block_shape():
+    """16x16 MFMA blocks exactly for the 4-wave 256x256 tile's 2-3 stage
+    direct rings with layout RC and int8/fp16/bf16; 32x32 everywhere else."""
+    for dtype in ("i8", "f16", "bf16", "f32"):
+        for layout in ("RC", "RR"):
+            for tile in ("256x256", "256x256w8", "128x128", "32x64"):
+                for stages in (1, 2, 3, 4):
+                    for variant in ("reg", "direct"):
+                        rc, info = q(dtype=dtype, layout=layout, stages=stages, variant=variant, tile=tile)
+                        if rc != binding.GEMM_OK:
+                            continue
+                        want16 = (tile == "256x256" and variant == "direct" and stages in (2, 3) and
+                                  layout == "RC" and dtype != "f32")
+                        assert info["mfma_block"] == (16 if want16 else 32), (dtype, layout, tile, stages, variant)
+
+
 def test_auto_tile_choice():
     assert q()[1]["tile"] == binding.GEMM_TILE_256x256                # 256 tiles of 256x256
     assert q(M=8192, N=64, K=8192)[1]["tile"] == binding.GEMM_TILE_32x64
