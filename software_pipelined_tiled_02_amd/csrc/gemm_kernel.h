@@ -24,8 +24,12 @@
 //    many tiles in flight in registers; STAGES = 1 is the skill's
 //    register-only prefetch into a single LDS buffer (two barriers per
 //    iteration), STAGES >= 2 use one barrier per iteration.
-// Both paths put a tile in LDS in the same swizzled layout and run the same
-// MFMA sequence, so every (STAGES, variant) pair gives bit-identical C.
+// Both paths put a tile in LDS in the same swizzled layout and add the same
+// k-slices in the same order, so every (STAGES, variant) pair gives the same
+// C.  The 256x256 tile's 2- and 3-stage direct RC instances build each
+// wave's block from 16x16 MFMA blocks instead of 32x32 (a higher sustained
+// clock); their results are bit-identical to the 32x32 instances -- exact for
+// int8, and measured bit for bit for fp16/bf16 by the GPU tests.
 //
 // MFMA mapping.  Both operands are read from LDS as one 16-byte chunk per
 // lane: lane l takes row (l % 32) of a 32-row fragment and chunk
