@@ -13,7 +13,9 @@
 // (lane l: row 16 h + l % 16, chunk c0 + l / 16).  The pair_i_j patterns
 // find which lanes one clock of a 16-byte read serves together: only lanes
 // i and j are active and read the same bank group 256 bytes apart, so the
-// read conflicts exactly when the two lanes share a clock.  Run it under
+// read conflicts exactly when the two lanes share a clock; trpair_i_j does
+// the same for the transposing read with every lane active (the others read
+// one broadcast piece).  Run it under
 //   rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS -- ./lds_layout_probe
 // and read the counters dispatch by dispatch in the order it prints.
 #include <hip/hip_runtime.h>
@@ -39,11 +41,11 @@ __global__ void __launch_bounds__(64) probe(const int* __restrict__ offs, int* o
     for (int i = threadIdx.x; i < kBytes / 16; i += 64) ((i32x4 LDSP*)raw)[i] = i32x4{i, i, i, i};
     __syncthreads();
     const int t = offs[threadIdx.x];                    // < 0: the lane takes no part
-    const int o = t & (kBytes - 16);                    // keeps every read inside the buffer
+    const int o = t & (kBytes - (TR ? 8 : 16));         // keeps every read inside the buffer, aligned
     int acc = 0;
     for (int r = 0; r < (t >= 0 ? kReps : 0); ++r) {
         if constexpr (TR) {
-            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDSP*)(raw + (o & ~7)));
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDSP*)(raw + o));
             acc += v[0] ^ v[3];
         } else {
             const i32x4 v = *(volatile i32x4 LDSP*)(raw + o);
@@ -135,6 +137,37 @@ int main() {
             p.off[j] = 256;
             pats.push_back(p);
         }
+
+    // The 16x16 blocks' B read of layout RR (bf16, 512-byte rows) under the
+    // kernels' RR swizzle: each 16-lane group g takes the same 16 columns at
+    // its own k rows 8g + j/4 (j = lane % 16), where the 32x32 read (above)
+    // splits the columns between groups and the k rows between half-waves.
+    {
+        const int rb = 512;
+        Pattern p{"rr16_tr16_rows512_xor", true, {}};
+        for (int l = 0; l < 64; ++l) {
+            const int g = l / 16, j = l % 16;
+            const int k = 8 * g + j / 4, n = 16 + 4 * (j & 3);
+            const int c = n * 2 / 16, b = n * 2 % 16;
+            p.off.push_back(k * rb + (c ^ swz_rr(DT_BF16, rb, k)) * 16 + b);
+        }
+        pats.push_back(p);
+    }
+    // Lane pairs of the transposing read: every lane active; all but lanes i
+    // and j read one 8-byte piece (a broadcast, bytes 8-15); lane i reads
+    // bytes 0-7, lane j bytes 512-519 (the same banks, 512 bytes on).
+    for (int i = 0; i < 64; i += 16)
+        for (int j = 0; j < 64; ++j) {
+            if (j == i) continue;
+            Pattern p{"trpair_" + std::to_string(i) + "_" + std::to_string(j), true, std::vector<int>(64, 8)};
+            p.off[i] = 0;
+            p.off[j] = 512;
+            pats.push_back(p);
+        }
+    {
+        Pattern p{"trpair_none", true, std::vector<int>(64, 8)};   // the broadcast alone
+        pats.push_back(p);
+    }
 
     int *d_off, *d_out;
     if (hipMalloc(&d_off, 64 * sizeof(int)) != hipSuccess || hipMalloc(&d_out, 64 * sizeof(int)) != hipSuccess) return 1;
