@@ -387,9 +387,20 @@ struct Gemm {
             for (int e = 0; e < 4; ++e) v[e] = *(const int PG_LDS*)(bt + ((k0 + e) * BN + n) * 4);
             return v;
         } else {
+            return tr_pair(bt + s.rrb[fn] + st * (2 * EPC) * RB_RR);
+        }
+    }
+    // 16x16 blocks: fragment idx covers columns wn*WTN + 16 idx; 16-lane
+    // group g holds k rows 4 st + g chunks in (s.rrb[idx] is the lane's
+    // offset for step 0; a step advances 4 chunks of k rows).
+    __device__ static __forceinline__ i32x4 read_b_rr16(const State& s, const uint8_t PG_LDS* bt, int idx, int st) {
+        return tr_pair(bt + s.rrb[idx] + st * (4 * EPC) * RB_RR);
+    }
+    // Two transposing reads, rr_rows_per_read k rows apart, at p.
+    __device__ static __forceinline__ i32x4 tr_pair(const uint8_t PG_LDS* p) {
+        {
             typedef int i32x2v __attribute__((ext_vector_type(2)));
             constexpr int RK = rr_rows_per_read(DT);            // k rows per transposing read
-            const uint8_t PG_LDS* p = bt + s.rrb[fn] + st * (2 * EPC) * RB_RR;
             i32x2v lo, hi;
             if constexpr (VARIANT == VAR_DIRECT) {
                 // With LDS-DMA writes in flight the compiler cannot tell that
@@ -559,6 +570,8 @@ struct Gemm {
         if (a_side)
             f.y[idx] = *(const i32x4 PG_LDS*)(smem + a_off(slot) + (s.wm * WTM + (idx >> 1) * 32) * CPR * kChunk +
                                               s.rd16[st][idx & 1]);
+        else if constexpr (RR)
+            f.x[idx] = read_b_rr16(s, smem + b_off(slot), idx, st);
         else
             f.x[idx] = *(const i32x4 PG_LDS*)(smem + b_off(slot) + (s.wn * WTN + (idx >> 1) * 32) * CPR * kChunk +
                                               s.rd16[st][idx & 1]);
@@ -581,6 +594,15 @@ struct Gemm {
         for (int u = 0; u < 64; ++u) {
             const int q = u / 16, i = u % 16;
             const int fm = (q >> 1) * 4 + i / 4, fn = (q & 1) * 4 + i % 4;
+            if constexpr (RR && VARIANT == VAR_DIRECT) {
+                // Layout RR's B reads are inline assembly (see tr_pair), so
+                // their waits are explicit: B 0-3 (read in the previous step)
+                // before the first quadrant; B 4-7 (read in the first
+                // quadrant, followed by exactly the 4 reads of A 4-7) before
+                // the second.  LDS reads complete in order.
+                if (u == 0) __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
+                if (u == 16) __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (4 << 8));
+            }
             acc[fm][fn] = mfma16<DT>(f.x[fn], f.y[fm], acc[fm][fn]);
             if (q == 0 && (i & 1) == 0) {
                 const int r = i / 2;                  // B 4-7, then A 4-7
@@ -858,7 +880,18 @@ struct Gemm {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
                     int k, n;
-                    if constexpr (SZ == 2) {
+                    if constexpr (B16) {
+                        // 16x16 blocks: group g takes the fragment's 16
+                        // columns at its own chunk g of k (the order the
+                        // K-contiguous read gives)
+                        if constexpr (SZ == 2) {
+                            k = 8 * g + jl / 4;
+                            n = s.wn * WTN + fn * 16 + 4 * (jl & 3);
+                        } else {
+                            k = 16 * g + jl / 2;
+                            n = s.wn * WTN + fn * 16 + 8 * (jl & 1);
+                        }
+                    } else if constexpr (SZ == 2) {
                         k = 8 * h + jl / 4;
                         n = s.wn * WTN + fn * 32 + 16 * (g & 1) + 4 * (jl & 3);
                     } else {

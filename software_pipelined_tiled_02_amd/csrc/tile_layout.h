@@ -83,12 +83,12 @@ constexpr int cpr_k(int tc, int stages, int variant) {
 constexpr int block_k(int dt, int tc, int stages, int variant) { return cpr_k(tc, stages, variant) * epc(dt); }
 
 // MFMA block edge: 16x16 blocks (16x16x32 fp16/bf16, 16x16x64 int8) for the
-// 4-wave 256x256 tile's 2-3 stage direct rings with K-contiguous B and
-// full-width K-tiles; 32x32 blocks for every other instance.  The matrix
+// 4-wave 256x256 tile's 2-3 stage direct rings with full-width K-tiles
+// (both layouts); 32x32 blocks for every other instance.  The matrix
 // cores hold a higher clock on the 16x16 blocks; both give the same bits.
 constexpr bool mfma_block16(int dt, int layout, int tc, int stages, int variant) {
     return tc == TILE_L && variant == VAR_DIRECT && stages >= 2 && cpr_k(tc, stages, variant) >= 8 &&
-           layout == LAYOUT_RC && dt != DT_F32;
+           (layout == LAYOUT_RC || layout == LAYOUT_RR) && dt != DT_F32;
 }
 
 // LDS slots of the ring and register staging sets per variant:
@@ -171,12 +171,22 @@ constexpr int swz(int cpr, int row) {
 // fragments are gathered element by element and are not swizzled.
 constexpr int rr_rows_per_read(int dt) { return dt == DT_I8 ? 8 : 4; }
 constexpr int rr_piece_bytes(int dt) { return dt == DT_I8 ? 32 : 64; }
+//
+// The transposing read is served in 2 clocks of 32 lanes (lanes 0-31, then
+// 32-63; measured).  With 16x16 MFMA blocks the two 16-lane groups of one
+// clock read the same 16 columns at k rows 2 * rr_rows_per_read apart (k
+// rows 0-3 and 8-11 for 16-bit types, 0-7 and 16-23 for 8-bit), which the
+// term above maps to the same banks; for rows of 256 bytes or more a second
+// term, in that k bit, moves the second group by half a row piece.  Every
+// clock of the 32x32 read takes k rows with equal bits there, so it stays
+// conflict-free.
 constexpr int swz_rr(int dt, int row_bytes, int k) {
     return dt == DT_F32 ? 0
          : ((k / (row_bytes >= 256 ? 1 : 256 / row_bytes))
             % (rr_rows_per_read(dt) / (row_bytes >= 256 ? 1 : 256 / row_bytes) > 0
                    ? rr_rows_per_read(dt) / (row_bytes >= 256 ? 1 : 256 / row_bytes) : 1))
-               * (rr_piece_bytes(dt) / kChunk);
+               * (rr_piece_bytes(dt) / kChunk)
+           ^ (row_bytes >= 256 ? ((k / (2 * rr_rows_per_read(dt))) & 1) * (rr_piece_bytes(dt) / kChunk / 2) : 0);
 }
 
 // Physical chunk index (within the tile) of logical (row, chunk).

@@ -179,6 +179,37 @@ int main() {
                                 if (!sw && worst > rr_raw) rr_raw = worst;
                             }
         }
+    // The 16x16 blocks' RR read (256x256 tile): 16-lane group g takes the
+    // fragment's 16 columns at its own k chunk, so one 32-lane clock reads
+    // the same columns at two k-row sets; the swizzle keeps it conflict-free.
+    {
+        const TileShape ts = tile_shape(TILE_L);
+        for (int dt = 0; dt < 3; ++dt) {
+            const int sz = in_size(dt), rb = ts.bn * sz, wtn = ts.bn / ts.wn;
+            for (int wn = 0; wn < ts.wn; ++wn)
+                for (int idx = 0; idx < wtn / 16; ++idx)
+                    for (int st = 0; st < 2; ++st)
+                        for (int r = 0; r < 2; ++r) {
+                            int worst = 1;
+                            for (int g0 = 0; g0 < 64; g0 += 32) {
+                                int hits[64] = {0};
+                                for (int l = g0; l < g0 + 32; ++l) {
+                                    const int g = l / 16, j = l % 16, nf = wn * wtn + idx * 16;
+                                    int k, n;
+                                    if (dt == DT_I8) { k = st * 64 + 16 * g + 8 * r + j / 2; n = nf + 8 * (j & 1); }
+                                    else { k = st * 32 + 8 * g + 4 * r + j / 4; n = nf + 4 * (j & 3); }
+                                    const int c = n * sz / kChunk, b = n * sz % kChunk;
+                                    const int addr = k * rb + (c ^ swz_rr(dt, rb, k)) * kChunk + b;
+                                    for (int w = 0; w < 2; ++w) {
+                                        const int bank = (addr / 4 + w) % 64;
+                                        if (++hits[bank] > worst) worst = hits[bank];
+                                    }
+                                }
+                            }
+                            if (worst != 1) { std::printf("RR 16x16 read conflicts: dt %d wn %d idx %d\n", dt, wn, idx); ++rr_fail; }
+                        }
+        }
+    }
     std::printf("RR transposing reads: swizzled %s, unswizzled worst %d-way\n", rr_fail ? "CONFLICTS" : "conflict-free", rr_raw);
     if (rr_raw == 1) ++rr_fail;
     fail += rr_fail;

@@ -127,7 +127,7 @@ def test_large_tile_budget(dtype, bk2, bk4):
 
 def test_mfma_block_shape():
     """16x16 MFMA blocks exactly for the 4-wave 256x256 tile's 2-3 stage
-    direct rings with layout RC and int8/fp16/bf16; 32x32 everywhere else."""
+    direct rings with int8/fp16/bf16 (both layouts); 32x32 everywhere else."""
     for dtype in ("i8", "f16", "bf16", "f32"):
         for layout in ("RC", "RR"):
             for tile in ("256x256", "256x256w8", "128x128", "32x64"):
@@ -137,7 +137,7 @@ def test_mfma_block_shape():
                         if rc != binding.GEMM_OK:
                             continue
                         want16 = (tile == "256x256" and variant == "direct" and stages in (2, 3) and
-                                  layout == "RC" and dtype != "f32")
+                                  dtype != "f32")
                         assert info["mfma_block"] == (16 if want16 else 32), (dtype, layout, tile, stages, variant)
 
 
