@@ -142,14 +142,16 @@ int main() {
     // kernels' RR swizzle: each 16-lane group g takes the same 16 columns at
     // its own k rows 8g + j/4 (j = lane % 16), where the 32x32 read (above)
     // splits the columns between groups and the k rows between half-waves.
-    {
+    // xorprev: the earlier RR swizzle of these rows, (k mod 4) x 4 chunks.
+    for (int lay = 0; lay < 2; ++lay) {
         const int rb = 512;
-        Pattern p{"rr16_tr16_rows512_xor", true, {}};
+        Pattern p{std::string("rr16_tr16_rows512") + (lay == 0 ? "_xor" : "_xorprev"), true, {}};
         for (int l = 0; l < 64; ++l) {
             const int g = l / 16, j = l % 16;
             const int k = 8 * g + j / 4, n = 16 + 4 * (j & 3);
             const int c = n * 2 / 16, b = n * 2 % 16;
-            p.off.push_back(k * rb + (c ^ swz_rr(DT_BF16, rb, k)) * 16 + b);
+            const int x = lay == 0 ? swz_rr(DT_BF16, rb, k) : (k % 4) * 4;
+            p.off.push_back(k * rb + (c ^ x) * 16 + b);
         }
         pats.push_back(p);
     }
