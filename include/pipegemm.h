@@ -131,8 +131,9 @@ typedef struct {
                                 grid = one workgroup per CU) */
     int32_t splits;          /* K splits per C tile (1: none); see gemm_run_splitk */
     int32_t mfma_block;      /* edge of the MFMA blocks the kernel uses: 16
-                                (256x256 tile, 2-3 direct stages, layout RC,
-                                int8/fp16/bf16) or 32; both give the same bits */
+                                (4-wave 256x256 tile, 2-3 direct stages, either
+                                layout, int8/fp16/bf16) or 32; both give the
+                                same bits */
     int64_t workspace_bytes; /* workspace gemm_run_splitk needs (0 when splits = 1) */
 } gemm_config_info_t;
 

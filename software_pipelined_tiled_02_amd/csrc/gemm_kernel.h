@@ -26,7 +26,7 @@
 //    iteration), STAGES >= 2 use one barrier per iteration.
 // Both paths put a tile in LDS in the same swizzled layout and add the same
 // k-slices in the same order, so every (STAGES, variant) pair gives the same
-// C.  The 256x256 tile's 2- and 3-stage direct RC instances build each
+// C.  The 256x256 tile's 2- and 3-stage direct instances build each
 // wave's block from 16x16 MFMA blocks instead of 32x32 (a higher sustained
 // clock); their results are bit-identical to the 32x32 instances -- exact for
 // int8, and measured bit for bit for fp16/bf16 by the GPU tests.
