@@ -61,13 +61,15 @@
  *
  * Memory ownership.  The caller allocates, owns and frees A, B, C and the
  * stream; they are device pointers (hipMalloc or torch CUDA tensors) on the
- * handle's device.  The library allocates no device memory.  A and B are
- * only read.  C must not overlap A or B.
+ * handle's device.  The library allocates no device memory; its code object
+ * holds one static array of GEMM_NOALLOC_SCRATCH_BYTES per device, the
+ * workspace of gemm_run_splitk_noalloc.  A and B are only read.  C must not
+ * overlap A or B.
  *
  * Errors.  Every entry point returns GEMM_OK (0) or one of the codes below;
  * nothing is thrown across the ABI.  Argument checks run before any HIP call,
- * so a rejected call has no side effect.  gemm_run and gemm_run_splitk are
- * asynchronous: each enqueues one kernel launch on `stream` (and nothing
+ * so a rejected call has no side effect.  gemm_run, gemm_run_splitk and
+ * gemm_run_splitk_noalloc are asynchronous: each enqueues one kernel launch on `stream` (and nothing
  * else, so a graph can capture it) and returns; faults during execution
  * surface at the caller's next synchronisation of that stream.
  */
@@ -95,9 +97,16 @@ enum {
                                   operand tile row span exceeds 2^31 bytes, or
                                   (gemm_run_splitk) more than one split with
                                   more than 16384 C tiles */
-    GEMM_ERR_HIP = 4           /* a HIP runtime call failed (no device, launch
+    GEMM_ERR_HIP = 4,          /* a HIP runtime call failed (no device, launch
                                   failure); see gemm_last_hip_error */
+    GEMM_ERR_SCRATCH = 5       /* gemm_run_splitk_noalloc: the split-K workspace
+                                  the call needs exceeds
+                                  GEMM_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the library's static scratch buffer (one per device), the
+ * workspace of gemm_run_splitk_noalloc: 32 MiB. */
+#define GEMM_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
 
 /* Tile classes selectable with gemm_set_tile.  GEMM_TILE_256x256_W8 is the
  * 256x256 tile run by 8 waves (2 per SIMD) instead of 4; it is never chosen
@@ -138,8 +147,12 @@ typedef struct {
 } gemm_config_info_t;
 
 /* Bind a handle to HIP device `device`.  Allocates host memory for the
- * handle only.  Returns GEMM_ERR_INVALID_ARG for a NULL `out` or a negative
- * device, GEMM_ERR_HIP when the device does not exist. */
+ * handle only.  The first call for a device also sets up that device's copy
+ * of the static scratch buffer of gemm_run_splitk_noalloc: it looks up its
+ * address and clears its arrival counters with one small kernel on the null
+ * stream, waiting for it (so call it outside any graph capture).  Returns
+ * GEMM_ERR_INVALID_ARG for a NULL `out` or a negative device, GEMM_ERR_HIP
+ * when the device does not exist or that set-up fails. */
 int gemm_create(gemm_handle_t *out, int device);
 
 /* C = A * B on `stream` (a hipStream_t; NULL is the null stream).  Argument
@@ -187,6 +200,28 @@ int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
                     const void *A, int64_t lda, const void *B, int64_t ldb,
                     void *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
                     void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * gemm_run_splitk with the library's own static scratch buffer as its
+ * workspace, so the caller passes no workspace and nothing is allocated.
+ *   Same arguments, checks and results as gemm_run_splitk (bit for bit:
+ * same kernels, same split count), without `workspace` / `workspace_bytes`.
+ * The buffer is a file-scope device array of GEMM_NOALLOC_SCRATCH_BYTES per
+ * device, held until the process ends; gemm_create sets it up for its
+ * device.  A call whose split-K workspace (info.workspace_bytes of
+ * gemm_query_splitk) exceeds that size returns GEMM_ERR_SCRATCH before any
+ * HIP call; with one split (splits = 1, or the automatic choice taking one)
+ * no scratch is used.  The call calls no hipMalloc, hipFree or allocating
+ * routine and enqueues one kernel launch on `stream`.
+ *   Every call on a device shares that device's buffer, which keeps the
+ * last call's contents; its arrival counters are zero after every completed
+ * call.  Calls that overlap on one device (e.g. on two streams) race on the
+ * buffer and must not be issued. */
+int gemm_run_splitk_noalloc(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                            int dtype, int layout, int stages, int variant, int splits,
+                            const void *A, int64_t lda, const void *B, int64_t ldb,
+                            void *C, int64_t ldc, void *stream);
 
 /* Release a handle.  NULL is a no-op.  Does not synchronise any stream. */
 int gemm_destroy(gemm_handle_t h);

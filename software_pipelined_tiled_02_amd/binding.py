@@ -15,6 +15,8 @@ GEMM_I8, GEMM_F16, GEMM_BF16, GEMM_F32 = 0, 1, 2, 3
 GEMM_LAYOUT_RR, GEMM_LAYOUT_RC = 0, 1
 GEMM_VARIANT_REG, GEMM_VARIANT_DIRECT = 0, 1
 GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_ALIGNMENT, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP = 0, 1, 2, 3, 4
+GEMM_ERR_SCRATCH = 5
+GEMM_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 GEMM_TILE_AUTO, GEMM_TILE_256x256, GEMM_TILE_128x128, GEMM_TILE_32x64, GEMM_TILE_256x256_W8 = -1, 0, 1, 2, 3
 
 DTYPES = {"i8": GEMM_I8, "f16": GEMM_F16, "bf16": GEMM_BF16, "f32": GEMM_F32}
@@ -25,7 +27,8 @@ TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_T
 
 # C functions exported by the library (the names include/pipegemm.h declares)
 EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",
-           "gemm_run_splitk", "gemm_query_splitk", "gemm_status_string", "gemm_last_hip_error")
+           "gemm_run_splitk", "gemm_query_splitk", "gemm_status_string", "gemm_last_hip_error",
+           "gemm_run_splitk_noalloc")
 
 
 class GemmError(RuntimeError):
@@ -73,6 +76,9 @@ def _lib():
         lib.gemm_run_splitk.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
                                         vp, i64, vp]
         lib.gemm_run_splitk.restype = ci
+        lib.gemm_run_splitk_noalloc.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp,
+                                                i64, vp]
+        lib.gemm_run_splitk_noalloc.restype = ci
         lib.gemm_query_splitk.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(ConfigInfo)]
         lib.gemm_query_splitk.restype = ci
@@ -149,6 +155,18 @@ def gemm_run_splitk(h, M, N, K, dtype, layout, stages, variant, splits, A, lda, 
                                 _ptr(C), ldc, _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and rc != GEMM_OK:
         raise GemmError(rc, "gemm_run_splitk")
+    return rc
+
+
+def gemm_run_splitk_noalloc(h, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb, C, ldc,
+                            stream=None, check=True):
+    """Enqueue C = A * B with K split over `splits` workgroups per C tile,
+    using the library's static scratch buffer (no workspace argument)."""
+    rc = _lib().gemm_run_splitk_noalloc(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
+                                        _enum(variant, VARIANTS), int(splits), _ptr(A), lda, _ptr(B), ldb,
+                                        _ptr(C), ldc, _stream(stream))
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_run_splitk_noalloc")
     return rc
 
 

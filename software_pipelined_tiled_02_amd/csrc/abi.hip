@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "pipegemm.h"
 #include "kernel_args.h"
 #include "tile_layout.h"
@@ -14,7 +16,17 @@ struct gemm_handle_s {
     int device;
     int num_cus;
     int tile_override;  // GEMM_TILE_AUTO or a class
+    void* scratch;      // this device's address of `scratch` (below)
 };
+
+// The split-K workspace of gemm_run_splitk_noalloc: one static array per
+// device, for callers that cannot allocate device memory.  In host code its
+// name is a host-side stand-in, not a device address: kernels get the
+// address hipGetSymbolAddress returns for the device (scratch_setup).  Its
+// first kSplitkCounterBytes are the arrival counters, cleared once per
+// device at set-up; every completed split-K call leaves them zero again.
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+static_assert(GEMM_NOALLOC_SCRATCH_BYTES > pg::kSplitkCounterBytes, "scratch holds the counters");
 
 namespace {
 
@@ -192,6 +204,91 @@ int hip_fail(hipError_t e) {
     return GEMM_ERR_HIP;
 }
 
+// Writes zeros over n 32-bit words (clears the scratch counters with a
+// kernel rather than a memset).
+__global__ void zero_words(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];   // per device: address of `scratch`, once set up
+
+// Once per device, with that device current: find this device's copy of
+// `scratch` and clear its arrival counters.  *out receives the address.
+hipError_t scratch_setup(int device, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (device >= kMaxDevices) return hipErrorInvalidDevice;
+    if (g_scratch[device] != nullptr) {
+        *out = g_scratch[device];
+        return hipSuccess;
+    }
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess) {
+        constexpr int words = (int)(pg::kSplitkCounterBytes / 4);
+        hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, nullptr, (uint32_t*)p, words);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    }
+    if (cur != device) {
+        const hipError_t r = hipSetDevice(cur);
+        if (e == hipSuccess) e = r;
+    }
+    if (e == hipSuccess) {
+        g_scratch[device] = p;
+        *out = p;
+    }
+    return e;
+}
+
+// Launch the instance `plan` chose on the handle's device (ws: the split-K
+// workspace when the plan has more than one split).
+int launch(gemm_handle_t h, const Plan& plan, int64_t M, int64_t N, int64_t K, int dtype, int layout,
+           int stages, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, void* ws,
+           void* stream) {
+    if (plan.info.grid == 0) return GEMM_OK;
+    const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
+    if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;
+
+    pg::GemmArgs args;
+    args.A = A;
+    args.B = B;
+    args.C = C;
+    args.lda = lda;
+    args.ldb = ldb;
+    args.ldc = ldc;
+    args.M = (int32_t)M;
+    args.N = (int32_t)N;
+    args.K = (int32_t)K;
+    args.tiles_m = (int32_t)plan.tiles_m;
+    args.tiles_n = (int32_t)plan.tiles_n;
+    args.splits = plan.info.splits;
+    args.ws = plan.info.splits > 1 ? ws : nullptr;
+
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess) return hip_fail(e);
+    void* kargs[] = {&args};
+    e = hipLaunchKernel(fn, dim3((unsigned)plan.info.grid), dim3((unsigned)plan.info.threads), kargs, 0,
+                        (hipStream_t)stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (cur != h->device) {
+        // put the caller's device back; a failure here is reported unless
+        // the launch itself already failed
+        const hipError_t r = hipSetDevice(cur);
+        if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -206,11 +303,15 @@ int gemm_create(gemm_handle_t* out, int device) {
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
     if (e != hipSuccess) return hip_fail(e);
+    void* scr = nullptr;
+    e = scratch_setup(device, &scr);
+    if (e != hipSuccess) return hip_fail(e);
     gemm_handle_s* h = new (std::nothrow) gemm_handle_s;
     if (h == nullptr) return GEMM_ERR_INVALID_ARG;
     h->device = device;
     h->num_cus = cus > 0 ? cus : kDefaultCus;
     h->tile_override = GEMM_TILE_AUTO;
+    h->scratch = scr;
     *out = h;
     return GEMM_OK;
 }
@@ -255,42 +356,19 @@ int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype,
         if (workspace == nullptr || workspace_bytes < plan.info.workspace_bytes) return GEMM_ERR_INVALID_ARG;
         if (((uintptr_t)workspace & 255u) != 0) return GEMM_ERR_ALIGNMENT;
     }
-    if (plan.info.grid == 0) return GEMM_OK;
+    return launch(h, plan, M, N, K, dtype, layout, stages, A, lda, B, ldb, C, ldc, workspace, stream);
+}
 
-    const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
-    if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;
-
-    pg::GemmArgs args;
-    args.A = A;
-    args.B = B;
-    args.C = C;
-    args.lda = lda;
-    args.ldb = ldb;
-    args.ldc = ldc;
-    args.M = (int32_t)M;
-    args.N = (int32_t)N;
-    args.K = (int32_t)K;
-    args.tiles_m = (int32_t)plan.tiles_m;
-    args.tiles_n = (int32_t)plan.tiles_n;
-    args.splits = plan.info.splits;
-    args.ws = plan.info.splits > 1 ? workspace : nullptr;
-
-    int cur = -1;
-    hipError_t e = hipGetDevice(&cur);
-    if (e != hipSuccess) return hip_fail(e);
-    if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess) return hip_fail(e);
-    void* kargs[] = {&args};
-    e = hipLaunchKernel(fn, dim3((unsigned)plan.info.grid), dim3((unsigned)plan.info.threads), kargs, 0,
-                        (hipStream_t)stream);
-    if (e == hipSuccess) e = hipGetLastError();
-    if (cur != h->device) {
-        // put the caller's device back; a failure here is reported unless
-        // the launch itself already failed
-        const hipError_t r = hipSetDevice(cur);
-        if (e == hipSuccess) e = r;
-    }
-    if (e != hipSuccess) return hip_fail(e);
-    return GEMM_OK;
+int gemm_run_splitk_noalloc(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout,
+                            int stages, int variant, int splits, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, void* C, int64_t ldc, void* stream) {
+    if (h == nullptr) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, A, lda, B, ldb, C,
+                       ldc, h->num_cus, false, &plan);
+    if (rc != GEMM_OK) return rc;
+    if (plan.info.workspace_bytes > (int64_t)GEMM_NOALLOC_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
+    return launch(h, plan, M, N, K, dtype, layout, stages, A, lda, B, ldb, C, ldc, h->scratch, stream);
 }
 
 int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
@@ -307,6 +385,9 @@ const char* gemm_status_string(int status) {
     case GEMM_ERR_ALIGNMENT: return "GEMM_ERR_ALIGNMENT: pointer, leading dimension or K not 16-byte aligned";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: no kernel instance for this configuration";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: HIP runtime error";
+    case GEMM_ERR_SCRATCH:
+        return "GEMM_ERR_SCRATCH: the split-K workspace this call needs exceeds the library's static scratch "
+               "buffer (GEMM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

@@ -157,7 +157,7 @@ def test_auto_tile_choice():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert binding.gemm_status_string(s).startswith("GEMM_")
     assert binding.gemm_status_string(99) == "unknown status"
 
@@ -222,3 +222,17 @@ def test_splitk_run_rejects_null_handle():
     rc = lib.gemm_run_splitk(None, 1024, 1024, 8192, 2, 1, 2, 1, 4, 16, 8192, 16, 8192, 16, 1024,
                              256, 1 << 30, None)
     assert rc == binding.GEMM_ERR_INVALID_ARG
+
+
+def test_splitk_noalloc_rejects_null_handle():
+    """gemm_run_splitk_noalloc checks its handle before anything else (its
+    scratch-size check needs a handle, i.e. a device, and is GPU-tested)."""
+    lib = binding.library()
+    rc = lib.gemm_run_splitk_noalloc(None, 1024, 1024, 8192, 2, 1, 2, 1, 4, 16, 8192, 16, 8192, 16, 1024, None)
+    assert rc == binding.GEMM_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert "#define GEMM_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)" in text
+    assert binding.GEMM_NOALLOC_SCRATCH_BYTES == 32 * 1024 * 1024
