@@ -246,6 +246,30 @@ int gemm_query_splitk(int64_t M, int64_t N, int64_t K, int dtype, int layout, in
                       const void *B, int64_t ldb, const void *C, int64_t ldc,
                       gemm_config_info_t *info);
 
+/* Resources and occupancy of the kernel instance gemm_run would launch for a
+ * call (see gemm_occupancy), the figures the "Part 4 -- Pipelining and
+ * Occupancy" page (section 4.2) reads from the occupancy calculator. */
+typedef struct {
+    int32_t blocks_per_cu;   /* hipOccupancyMaxActiveBlocksPerMultiprocessor at
+                                the instance's block size (no dynamic LDS) */
+    int32_t waves_per_cu;    /* blocks_per_cu x waves per block (4 SIMDs per CU) */
+    int32_t num_regs;        /* hipFuncGetAttributes numRegs: vector registers
+                                per lane as the runtime reports them */
+    int32_t lds_bytes;       /* static LDS per workgroup (sharedSizeBytes) */
+    int32_t scratch_bytes;   /* private scratch per lane (localSizeBytes; 0 =
+                                no register spill) */
+    int32_t threads;         /* per workgroup */
+} gemm_occupancy_t;
+
+/* The occupancy of the instance gemm_run would launch on this handle (its
+ * tile override, its device) for a call of this shape, dtype, layout,
+ * stages and variant; pointers are not needed (the checks of gemm_query).
+ * Makes HIP calls (function attributes, occupancy) on the handle's device;
+ * launches nothing.  Errors: those of gemm_query, GEMM_ERR_INVALID_ARG for a
+ * NULL handle or `out`, GEMM_ERR_HIP when a HIP call fails. */
+int gemm_occupancy(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout,
+                   int stages, int variant, gemm_occupancy_t *out);
+
 /* Static text for a status code (never NULL). */
 const char *gemm_status_string(int status);
 

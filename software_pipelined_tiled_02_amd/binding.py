@@ -28,7 +28,7 @@ TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_T
 # C functions exported by the library (the names include/pipegemm.h declares)
 EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",
            "gemm_run_splitk", "gemm_query_splitk", "gemm_status_string", "gemm_last_hip_error",
-           "gemm_run_splitk_noalloc")
+           "gemm_run_splitk_noalloc", "gemm_occupancy")
 
 
 class GemmError(RuntimeError):
@@ -47,6 +47,14 @@ class ConfigInfo(ctypes.Structure):
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
         ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("mfma_block", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class Occupancy(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "blocks_per_cu", "waves_per_cu", "num_regs", "lds_bytes", "scratch_bytes", "threads")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -79,6 +87,8 @@ def _lib():
         lib.gemm_run_splitk_noalloc.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp,
                                                 i64, vp]
         lib.gemm_run_splitk_noalloc.restype = ci
+        lib.gemm_occupancy.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ctypes.POINTER(Occupancy)]
+        lib.gemm_occupancy.restype = ci
         lib.gemm_query_splitk.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
                                           ctypes.POINTER(ConfigInfo)]
         lib.gemm_query_splitk.restype = ci
@@ -168,6 +178,16 @@ def gemm_run_splitk_noalloc(h, M, N, K, dtype, layout, stages, variant, splits, 
     if check and rc != GEMM_OK:
         raise GemmError(rc, "gemm_run_splitk_noalloc")
     return rc
+
+
+def gemm_occupancy(h, M, N, K, dtype, layout, stages, variant):
+    """Resources and occupancy of the instance gemm_run would launch (a dict)."""
+    out = Occupancy()
+    rc = _lib().gemm_occupancy(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
+                               _enum(variant, VARIANTS), ctypes.byref(out))
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_occupancy")
+    return out.as_dict()
 
 
 def gemm_query(M, N, K, dtype, layout, stages, variant, tile="auto", A=0, lda=None, B=0,

@@ -378,6 +378,39 @@ int gemm_run(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int la
                            stream);
 }
 
+int gemm_occupancy(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+                   int variant, gemm_occupancy_t* out) {
+    if (h == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    const int64_t ldb = layout == GEMM_LAYOUT_RR ? N : K;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, 1, nullptr, K, nullptr, ldb,
+                       nullptr, N, h->num_cus, true, &plan);
+    if (rc != GEMM_OK) return rc;
+    const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
+    if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess) return hip_fail(e);
+    hipFuncAttributes fa;
+    int blocks = 0;
+    e = hipFuncGetAttributes(&fa, fn);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, plan.info.threads, 0);
+    if (cur != h->device) {
+        const hipError_t r = hipSetDevice(cur);
+        if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+    memset(out, 0, sizeof *out);
+    out->blocks_per_cu = blocks;
+    out->waves_per_cu = blocks * (plan.info.threads / 64);
+    out->num_regs = fa.numRegs;
+    out->lds_bytes = (int32_t)fa.sharedSizeBytes;
+    out->scratch_bytes = (int32_t)fa.localSizeBytes;
+    out->threads = plan.info.threads;
+    return GEMM_OK;
+}
+
 const char* gemm_status_string(int status) {
     switch (status) {
     case GEMM_OK: return "GEMM_OK";

@@ -17,7 +17,8 @@
 // s_memtime against the fixed 100 MHz s_memrealtime, and with it the share of
 // cycles the matrix cores are busy (rate / (per-clock datasheet rate x clock)).
 // A third figure (prefix mfma16_) runs the LDS-fed loop with 16x16 MFMA
-// blocks, which the GEMM does not use.
+// blocks, the GEMM's 256x256 2-3 stage direct instances' block shape, with
+// the MFMA written as the GEMM writes it (tied inline assembly).
 //
 // HBM ceiling.  A 1 GiB buffer (four times the Infinity Cache) read once with
 // 16-byte loads, each workgroup sweeping one contiguous block; the same
@@ -152,17 +153,23 @@ __global__ void __launch_bounds__(256) mfma_ceiling(int iters, int* out, unsigne
 // int8): 8 x 8 blocks per wave cover the same 128 x 128 accumulator tile, and
 // each k-step reads 16 fragments for 64 MFMAs -- the same LDS bytes per
 // multiply-add as the 32x32 loop.  Operands from LDS, read one step ahead.
+//   The MFMA is written as the GEMM writes it: inline assembly with the
+// accumulator tied in place in AGPRs.  (With the compiler's builtins the
+// int8 loop moved its accumulators between registers at every step -- over
+// 500 accvgpr moves per iteration -- and measured the copies, 75% busy.)
+// The compiler sees no MFMA in these, so the kernel pads the hazards itself:
+// a few wait states after the accumulators are set and before the first
+// MFMA, and more than any MFMA result needs before they are read.
 template <int DT>
 __device__ __forceinline__ i32x4 mma16(i32x4 x, i32x4 y, i32x4 c) {
     if constexpr (DT == I8) {
-        return __builtin_amdgcn_mfma_i32_16x16x64_i8(x, y, c, 0, 0, 0);
+        asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     } else if constexpr (DT == BF16) {
-        return __builtin_bit_cast(i32x4, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), __builtin_bit_cast(f32x4, c), 0, 0, 0));
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     } else {
-        return __builtin_bit_cast(i32x4, __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), __builtin_bit_cast(f32x4, c), 0, 0, 0));
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y));
     }
+    return c;
 }
 
 template <int DT>
@@ -202,9 +209,11 @@ __global__ void __launch_bounds__(256) mfma16_ceiling(int iters, int* out, unsig
     }
     const unsigned long long t0 = __builtin_readcyclecounter(), r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; it += 2) {   // iters is even
+        asm volatile("s_nop 4" ::: "memory");   // accumulators set by ordinary moves before the loop
         probe_step16<DT>(acc, x0, y0, x1, y1, lds, it + 1, lane);
         probe_step16<DT>(acc, x1, y1, x0, y0, lds, it + 2, lane);
     }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");   // last MFMA results before they are read
     const unsigned long long t1 = __builtin_readcyclecounter(), r1 = __builtin_amdgcn_s_memrealtime();
     int s = 0;
     for (int a = 0; a < 8; ++a)

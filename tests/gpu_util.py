@@ -111,6 +111,19 @@ def oracle_full(a_cpu, b_cpu, dtype, layout):
     return oracle.gemm(inputs.to_oracle(a_cpu, dtype), inputs.to_oracle(b_cpu, dtype), dtype, layout)
 
 
+def oracle_full_widened(a_cpu, b_cpu, dtype, layout):
+    """oracle_full for large fp16/bf16 shapes through the oracle's fp32
+    entry: every fp16 and bf16 value is exactly an fp32 value (torch's
+    widening is exact), and the oracle decodes both encodings exactly to
+    double and then does the same double arithmetic in the same k order, so
+    the result is the same doubles, bit for bit (pinned on the CPU by
+    tests/test_oracle.py) -- only the per-element decoding, which dominates
+    the oracle's time for fp16, is skipped.  Other dtypes: oracle_full."""
+    if dtype not in ("f16", "bf16"):
+        return oracle_full(a_cpu, b_cpu, dtype, layout)
+    return oracle.gemm(a_cpu.float().contiguous().numpy(), b_cpu.float().contiguous().numpy(), "f32", layout)
+
+
 def check_close(c_gpu, ref, dtype, what=""):
     """Assert the pages' tolerance for dtype; returns (max_abs_err, frob_rel)."""
     got = inputs.from_torch_out(c_gpu, dtype)

@@ -236,3 +236,10 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     assert "#define GEMM_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)" in text
     assert binding.GEMM_NOALLOC_SCRATCH_BYTES == 32 * 1024 * 1024
+
+
+def test_occupancy_rejects_null_handle():
+    lib = binding.library()
+    out = binding.Occupancy()
+    import ctypes
+    assert lib.gemm_occupancy(None, 256, 256, 256, 3, 0, 2, 0, ctypes.byref(out)) == binding.GEMM_ERR_INVALID_ARG

@@ -85,3 +85,34 @@ def test_pins_catch_planted_mistake(desc, old, new, count):
         assert failed, "no pin caught: " + desc
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", ["RR", "RC"])
+def test_widened_inputs_give_the_same_doubles(orc, dtype, layout):
+    """The full-size GPU parity tests call the oracle's fp32 entry on fp16 /
+    bf16 operands widened to fp32 (exact): it must return exactly the
+    doubles of the fp16 / bf16 entry.  Inputs cover subnormals, signed
+    zeros, the largest finite values and ordinary values."""
+    import torch
+    from software_pipelined_tiled_02_amd import inputs
+    rng = np.random.default_rng(7)
+    M, N, K = 37, 29, 301
+    tdt = inputs.TORCH_DTYPES[dtype]
+    special = {"f16": [0x0001, 0x03FF, 0x8001, 0x7BFF, 0xFBFF, 0x8000, 0x0000, 0x3C00],
+               "bf16": [0x0001, 0x007F, 0x8001, 0x7F7F, 0xFF7F, 0x8000, 0x0000, 0x3F80]}[dtype]
+
+    def draw(shape):
+        bits = rng.integers(0, 65536, size=shape, dtype=np.int64)
+        x = torch.from_numpy(bits.astype(np.int16)).view(tdt)
+        bad = ~torch.isfinite(x.float())
+        x[bad] = 0.5                                   # no inf / NaN operands
+        flat = x.view(-1)
+        flat[: len(special)] = torch.tensor(np.array(special, dtype=np.int64).astype(np.int16)).view(tdt)
+        return x.contiguous()
+
+    a = draw((M, K))              # products and sums stay finite in double
+    b = draw((K, N) if layout == "RR" else (N, K))
+    ref = orc.gemm(inputs.to_oracle(a, dtype), inputs.to_oracle(b, dtype), dtype, layout)
+    wid = orc.gemm(a.float().contiguous().numpy(), b.float().contiguous().numpy(), "f32", layout)
+    assert np.array_equal(ref.view(np.int64), wid.view(np.int64))
