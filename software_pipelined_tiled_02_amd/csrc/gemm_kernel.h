@@ -152,6 +152,16 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
+// Every global load and LDS access of this wave has completed.  After the
+// direct variant's K loop: no LDS-DMA write may outlive the loop, and the
+// last hand-over's fragment reads (in layout RR inline assembly, which the
+// compiler does not track) must land before their registers are reused.
+__device__ __forceinline__ void wait_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((0) | (0 << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+}
+
 // Workgroup barrier that also drains this wave's LDS accesses first.
 __device__ __forceinline__ void block_sync() {
     asm volatile("" ::: "memory");
@@ -874,30 +884,14 @@ struct Gemm {
             }
             s.kb_step = (uint32_t)BK * ldb_b;
             if constexpr (SZ != 4) {
-                // Transposing reads: lane j of each 16-lane group g supplies
-                // the piece of row k at column n (see tile_layout.h).
-                const int h = lane >> 5, g = lane >> 4, jl = lane & 15;
+                // Transposing reads: each lane supplies the piece of row k
+                // at column n (rr_lane_k / rr_lane_n; 16x16 blocks: group g
+                // takes the fragment's 16 columns at its own chunk g of k,
+                // the order the K-contiguous read gives).
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
-                    int k, n;
-                    if constexpr (B16) {
-                        // 16x16 blocks: group g takes the fragment's 16
-                        // columns at its own chunk g of k (the order the
-                        // K-contiguous read gives)
-                        if constexpr (SZ == 2) {
-                            k = 8 * g + jl / 4;
-                            n = s.wn * WTN + fn * 16 + 4 * (jl & 3);
-                        } else {
-                            k = 16 * g + jl / 2;
-                            n = s.wn * WTN + fn * 16 + 8 * (jl & 1);
-                        }
-                    } else if constexpr (SZ == 2) {
-                        k = 8 * h + jl / 4;
-                        n = s.wn * WTN + fn * 32 + 16 * (g & 1) + 4 * (jl & 3);
-                    } else {
-                        k = 16 * h + jl / 2;
-                        n = s.wn * WTN + fn * 32 + 16 * (g & 1) + 8 * (jl & 1);
-                    }
+                    const int k = rr_lane_k(DT, B16, lane);
+                    const int n = s.wn * WTN + fn * BS + rr_lane_n(DT, B16, lane);
                     const int c = n * SZ / kChunk, b = n * SZ % kChunk;
                     s.rrb[fn] = (uint32_t)(k * RB_RR + (c ^ swz_rr(DT, RB_RR, k)) * kChunk + b);
                 }
@@ -964,7 +958,7 @@ struct Gemm {
                 block_sync();
                 issue_direct<0, LPT>(s, smem, kt + 1, 0);
             }
-            wait_vmcnt<0>();   // no LDS write may outlive the loop
+            wait_all();   // no LDS write or fragment read may outlive the loop
         } else if constexpr (VARIANT == VAR_DIRECT) {
             // Ring of STAGES slots: while tile kt is multiplied, tiles
             // kt+1 .. kt+STAGES-1 are in flight; tile kt+STAGES-1 goes into
@@ -1017,7 +1011,7 @@ struct Gemm {
                 slot = next;
             }
             }
-            wait_vmcnt<0>();   // no LDS write may outlive the loop
+            wait_all();   // no LDS write or fragment read may outlive the loop
         } else {
             i32x4 regs[RSETS][LPT];
             if constexpr (STAGES == 1) {
@@ -1072,6 +1066,11 @@ struct Gemm {
         // instruction then writes whole rows of the wave's block, 16 bytes
         // per lane.  The ring is free once every wave has drained its loads
         // and crossed the barrier below.
+        //   2-byte outputs: a lane's converted values are 8 bytes per block
+        // and step; a lane swap (v_permlane16/32_swap) pairs two lanes'
+        // pieces so that each lane holds 16 consecutive bytes of one row,
+        // written with one 16-byte LDS write at strip_off (8-byte writes
+        // measured bank conflicts in every layout).
         block_sync();
         const int t = lane & 31, h = lane >> 5;
         const int mw = m0 + s.wm * WTM, nw = n0 + s.wn * WTN;
@@ -1081,47 +1080,52 @@ struct Gemm {
         for (int fm = 0; fm < (B16 ? FM / 2 : FM); ++fm) {   // 32-row strips
             if constexpr (B16) {
                 // 16x16 blocks 2 fm and 2 fm + 1: lane l holds row (l % 16),
-                // columns 4 (l / 16) .. +3 of each; the same strip layout
-                // (2-byte outputs: 8-byte halves swapped in rows 8-15, 24-31).
+                // columns 4 (l / 16) .. +3 of each.
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
+                for (int half = 0; half < 2; ++half) {
+                    const int row = 16 * half + (lane & 15), g = lane >> 4;
+                    if constexpr (OSZ == 4) {
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn) {
-                        const int row = 16 * half + (lane & 15), g = lane >> 4;
-                        const acc_t a = acc[2 * fm + half][fn];
-                        if constexpr (OSZ == 4) {
-                            *(i32x4 PG_LDS*)(strip + row * STRIP_ROW + (fn * 16 + 4 * g) * 4) = a;
-                        } else {
-                            const f32x4 af = __builtin_bit_cast(f32x4, a);   // whole vector, then index
-                            const int hs = (g & 1) ^ ((row >> 3) & 1);
-                            *(i32x2 PG_LDS*)(strip + row * STRIP_ROW + (fn * 16 + 8 * (g >> 1)) * 2 + 8 * hs) =
-                                cvt4_16(af[0], af[1], af[2], af[3]);
+                        for (int fn = 0; fn < FN; ++fn)
+                            *(i32x4 PG_LDS*)(strip + row * STRIP_ROW + (fn * 16 + 4 * g) * 4) = acc[2 * fm + half][fn];
+                    } else {
+                        // Blocks 2p and 2p + 1: after the swap (odd 16-lane
+                        // groups' first block with even groups' second),
+                        // group g holds columns 8 (g / 2) .. +7 of block
+                        // 2p + (g % 2), i.e. 16-byte chunk 4p + 2 (g % 2) + g / 2.
+#pragma unroll
+                        for (int pb = 0; pb < FN / 2; ++pb) {
+                            const f32x4 x = __builtin_bit_cast(f32x4, acc[2 * fm + half][2 * pb]);   // whole vector, then index
+                            const f32x4 y = __builtin_bit_cast(f32x4, acc[2 * fm + half][2 * pb + 1]);
+                            const i32x4 v = swap_pair<16>(cvt4_16(x[0], x[1], x[2], x[3]), cvt4_16(y[0], y[1], y[2], y[3]));
+                            *(i32x4 PG_LDS*)(strip + strip_off(CPRS, row, epi16_chunk(pb, g))) = v;
                         }
                     }
+                }
             } else
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn) {
+                if constexpr (OSZ == 4) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if constexpr (OSZ == 4) {
+                    for (int q = 0; q < 4; ++q)
                         *(i32x4 PG_LDS*)(strip + t * STRIP_ROW + (fn * 32 + 8 * q + 4 * h) * 4) = out4_32(acc[fm][fn], q);
-                    } else {
-                        // Rows 8..15 and 24..31 keep the two 8-byte halves
-                        // of each 16-byte chunk swapped: with rows 32 bytes
-                        // apart (mod 256), rows t and t+8 then fill the
-                        // complementary halves of the same banks.
-                        const int hs = h ^ ((t >> 3) & 1);
-                        *(i32x2 PG_LDS*)(strip + t * STRIP_ROW + (fn * 32 + 8 * q) * 2 + 8 * hs) = out4_16(acc[fm][fn], q);
+                } else {
+                    // q = 2j and 2j + 1: after the swap (upper half-wave's
+                    // first with lower half-wave's second) half-wave h holds
+                    // columns 8 (2j + h) .. +7, i.e. 16-byte chunk 4 fn + 2j + h.
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const i32x4 v = swap_pair<32>(out4_16(acc[fm][fn], 2 * j), out4_16(acc[fm][fn], 2 * j + 1));
+                        *(i32x4 PG_LDS*)(strip + strip_off(CPRS, t, epi32_chunk(fn, j, h))) = v;
                     }
                 }
+            }
 #pragma unroll
             for (int i = 0; i < 32 / ROWS_PER_STORE; ++i) {
                 const int r = i * ROWS_PER_STORE + lane / LANES_PER_ROW;
-                const int c = (lane % LANES_PER_ROW) * (kChunk / OSZ);   // column in the wave block
-                i32x4 v = *(const i32x4 PG_LDS*)(strip + r * STRIP_ROW + c * OSZ);
-                if constexpr (OSZ == 2) {
-                    if ((r >> 3) & 1) v = i32x4{v[2], v[3], v[0], v[1]};
-                }
+                const int cc = lane % LANES_PER_ROW;                       // 16-byte chunk of the row
+                const int c = cc * (kChunk / OSZ);                          // column in the wave block
+                const i32x4 v = *(const i32x4 PG_LDS*)(strip + (OSZ == 2 ? strip_off(CPRS, r, cc) : r * STRIP_ROW + cc * kChunk));
                 const int m = mw + fm * 32 + r, n = nw + c;
                 uint8_t* dst = (uint8_t*)args.C + ((int64_t)m * args.ldc + n) * OSZ;
                 if (full) {
@@ -1134,11 +1138,33 @@ struct Gemm {
         }
     }
 
-    // Staging strip of the epilogue: 32 rows of one wave's block, each row
-    // padded so that the rows written at one column fall in different LDS
-    // banks (see strip_row_bytes).
+    // Two lanes' 8-byte pieces into one lane's 16 bytes: x and y are the
+    // lane's pieces of two blocks (steps); v_permlane<W>_swap exchanges the
+    // odd W-lane groups' x with the even groups' y, so even groups return
+    // (x, x of the next group) and odd groups (y of the previous group, y).
+    template <int W>
+    __device__ static __forceinline__ i32x4 swap_pair(i32x2 x, i32x2 y) {
+        uint32_t a0 = (uint32_t)x[0], a1 = (uint32_t)x[1], b0 = (uint32_t)y[0], b1 = (uint32_t)y[1];
+        if constexpr (W == 16) {
+            const auto r0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+            const auto r1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+            a0 = r0[0]; b0 = r0[1]; a1 = r1[0]; b1 = r1[1];
+        } else {
+            const auto r0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+            a0 = r0[0]; b0 = r0[1]; a1 = r1[0]; b1 = r1[1];
+        }
+        return i32x4{(int)a0, (int)a1, (int)b0, (int)b1};
+    }
+
+    // Staging strip of the epilogue: 32 rows of one wave's block; 4-byte
+    // outputs in rows padded so that the rows written at one column fall in
+    // different LDS banks (see strip_row_bytes), 2-byte outputs placed by
+    // strip_off.
     static constexpr int STRIP_ROW = strip_row_bytes(DT, TC);
     static constexpr int STRIP_BYTES = 32 * STRIP_ROW;
+    static constexpr int CPRS = WTN * OSZ / kChunk;     // 16-byte chunks per strip row
+    static_assert(OSZ == 4 || CPRS == 16 || CPRS == 8 || CPRS == 4, "2-byte strip layout");
     static constexpr int LANES_PER_ROW = WTN * OSZ / kChunk;
     static constexpr int ROWS_PER_STORE = 64 / LANES_PER_ROW;
     static_assert(64 % LANES_PER_ROW == 0 && 32 % ROWS_PER_STORE == 0, "epilogue store shape");

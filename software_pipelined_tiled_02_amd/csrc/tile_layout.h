@@ -115,13 +115,12 @@ constexpr int ring_bytes(int dt, int tc, int stages, int variant) {
                ? (3 * tile_shape(tc).bm + 2 * tile_shape(tc).bn) * block_k(dt, tc, stages, variant) * in_size(dt)
                : slot_bytes(dt, tc, stages, variant) * lds_slots(variant, stages);
 }
-// The epilogue reuses LDS to stage one 32-row strip of C per wave; a strip
-// row is the wave's block width plus padding that spreads the rows over the
-// LDS banks: 16 bytes for 4-byte outputs (16-byte stores, one row per lane),
-// 32 bytes for 2-byte outputs (each lane stores two 8-byte pieces 16 bytes
-// apart, so consecutive rows must start 32 bytes apart).
+// The epilogue reuses LDS to stage one 32-row strip of C per wave.  A strip
+// row is the wave's block width, plus 16 bytes of padding that spreads the
+// rows over the LDS banks for 4-byte outputs; 2-byte outputs are placed by
+// strip_off instead (no padding).
 constexpr int strip_row_bytes(int dt, int tc) {
-    return tile_shape(tc).bn / tile_shape(tc).wn * out_size(dt) + (out_size(dt) == 2 ? 2 * kChunk : kChunk);
+    return tile_shape(tc).bn / tile_shape(tc).wn * out_size(dt) + (out_size(dt) == 2 ? 0 : kChunk);
 }
 constexpr int epilogue_bytes(int dt, int tc) {
     return 32 * strip_row_bytes(dt, tc) * tile_shape(tc).wm * tile_shape(tc).wn;
@@ -170,6 +169,20 @@ constexpr int swz(int cpr, int row) {
 // row so that these 4 or 8 row pieces land in different banks.  fp32 B
 // fragments are gathered element by element and are not swizzled.
 constexpr int rr_rows_per_read(int dt) { return dt == DT_I8 ? 8 : 4; }
+// The (k row, n column) of the 8-byte piece lane l supplies to the first
+// transposing read of a B fragment, relative to the fragment's first column
+// and the step's first k row.  32x32 blocks: half-wave h = l / 32 takes k
+// rows from 8 h (16-bit types) / 16 h (int8), 16-lane groups g = l / 16
+// alternate between the fragment's two 16-column halves; 16x16 blocks: each
+// group g takes the fragment's 16 columns at its own k chunk, rows 8 g /
+// 16 g on.  The second read of the pair is rr_rows_per_read rows further.
+constexpr int rr_lane_k(int dt, bool b16, int l) {
+    return dt == DT_I8 ? (b16 ? 16 * (l >> 4) : 16 * (l >> 5)) + (l & 15) / 2
+                       : (b16 ? 8 * (l >> 4) : 8 * (l >> 5)) + (l & 15) / 4;
+}
+constexpr int rr_lane_n(int dt, bool b16, int l) {
+    return (b16 ? 0 : 16 * ((l >> 4) & 1)) + (dt == DT_I8 ? 8 * (l & 1) : 4 * (l & 3));
+}
 constexpr int rr_piece_bytes(int dt) { return dt == DT_I8 ? 32 : 64; }
 //
 // The transposing read is served in 2 clocks of 32 lanes (lanes 0-31, then
@@ -187,6 +200,36 @@ constexpr int swz_rr(int dt, int row_bytes, int k) {
                    ? rr_rows_per_read(dt) / (row_bytes >= 256 ? 1 : 256 / row_bytes) : 1))
                * (rr_piece_bytes(dt) / kChunk)
            ^ (row_bytes >= 256 ? ((k / (2 * rr_rows_per_read(dt))) & 1) * (rr_piece_bytes(dt) / kChunk / 2) : 0);
+}
+
+// Epilogue strip of 2-byte outputs: 32 rows of a wave's block, each row
+// `cprs` (16, 8 or 4) 16-byte chunks, no padding, written and read in whole
+// chunks (ds_write_b128 / ds_read_b128).  The strip is a run of 256-byte
+// bank lines (16 slots of 16 bytes), 16 / cprs rows per line.  Measured on
+// gfx950 (lds_layout_probe): a 16-byte write is served 8 consecutive lanes
+// per clock, and the clock is conflict-free when their 8 chunks fill one
+// 128-byte half of the line's slots (slots 0-7 or 8-15) -- 8 distinct slots
+// spread over both halves still cost a cycle; a 16-byte read 16 lanes per
+// clock (lanes 2 (l / 32) + the parity of bits 2-4 of l), conflict-free when
+// they reach 16 different slots.  The writes put 8 consecutive rows' copies
+// of one chunk index in a clock; the read-back reads whole rows.
+// strip_off gives the byte offset of chunk c of row r so that both are
+// conflict-free (checked on the host against these models and measured):
+//   cprs 16: one row per line, chunk c ^ (r mod 16);
+//   cprs 8:  rows 2m, 2m+1 share line m; chunks 0-3 in the first half,
+//            4-7 in the second, slot 2 ((c mod 4) ^ (m mod 4)) + (r mod 2);
+//   cprs 4:  rows 4m .. 4m+3 share line m; chunks 0-1 in the first half,
+//            2-3 in the second, slot (2 (r mod 4) + (c mod 2)) ^ (m mod 2).
+// The 16-byte chunk each lane writes once the epilogue's lane swap has
+// paired its 8-byte pieces: 16x16 blocks, pair pb of blocks (2 pb, 2 pb + 1),
+// 16-lane group g (columns 8 (g / 2) .. +7 of block 2 pb + g % 2); 32x32
+// blocks, block fn, step pair j (steps 2j, 2j+1), half-wave h.
+constexpr int epi16_chunk(int pb, int g) { return 4 * pb + 2 * (g & 1) + (g >> 1); }
+constexpr int epi32_chunk(int fn, int j, int h) { return 4 * fn + 2 * j + h; }
+constexpr int strip_off(int cprs, int row, int c) {
+    return cprs == 16 ? row * 256 + ((c ^ (row & 15)) * 16)
+         : cprs == 8  ? (row >> 1) * 256 + (8 * (c >> 2) + 2 * ((c & 3) ^ ((row >> 1) & 3)) + (row & 1)) * 16
+                      : (row >> 2) * 256 + (8 * (c >> 1) + (((row & 3) * 2 + (c & 1)) ^ ((row >> 2) & 1))) * 16;
 }
 
 // Physical chunk index (within the tile) of logical (row, chunk).

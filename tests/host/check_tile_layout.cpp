@@ -14,9 +14,13 @@
 //  3. without the swizzle the same read does conflict (so 2 is not vacuous);
 //  4. the transposing reads of layout RR's B tile are conflict-free;
 //  5. the K-tile order is a permutation with the ragged tile in the
-//     prologue, and every stage count adds the k-slices in one order.
+//     prologue, and every stage count adds the k-slices in one order;
+//  6. the epilogue strips of 2-byte outputs (strip_off) are written with
+//     16-byte writes and read back without bank conflicts (the measured
+//     8-lane write clocks, the 16-lane read clocks above).
 // Prints one line per chunks-per-row value; exits non-zero on failure.
 #include <cstdio>
+#include <initializer_list>
 #include "tile_layout.h"
 
 using namespace pg;
@@ -58,6 +62,31 @@ static void read_offsets(int cpr, int lay, bool wide, int rb, int c0, int h, int
                 : lay == 1 ? row * (cpr * 16 + 16) + chunk * 16
                            : phys_chunk(cpr, row, chunk) * 16;
     }
+}
+
+// Extra clocks of one 16-byte write (ds_write_b128) whose lane l writes
+// offs[l] (< 0: lane off).  As measured: 8 consecutive lanes per clock; a
+// clock takes one pass per 128-byte half of the 256-byte bank line its
+// chunks touch, times the most distinct addresses any 16-byte slot is asked
+// for.
+static int write_extra_clocks(const int (&offs)[64]) {
+    int total = 0;
+    for (int k = 0; k < 8; ++k) {
+        int addr[16][8], n[16] = {0}, worst = 0;
+        bool half[2] = {false, false};
+        for (int l = 8 * k; l < 8 * k + 8; ++l) {
+            if (offs[l] < 0) continue;
+            const int g = (offs[l] / 16) % 16;
+            half[g / 8] = true;
+            bool seen = false;
+            for (int i = 0; i < n[g]; ++i) seen |= addr[g][i] == offs[l];
+            if (!seen) addr[g][n[g]++] = offs[l];
+            if (n[g] > worst) worst = n[g];
+        }
+        const int passes = (half[0] ? 1 : 0) + (half[1] ? 1 : 0);
+        if (worst > 0) total += passes * worst - 1;
+    }
+    return total;
 }
 
 static int conflict_cycles(int cpr, int lay, bool wide, int rb, int c0, int h) {
@@ -119,6 +148,62 @@ int main() {
                 extra_clocks(prev) != 4) { std::printf("model off: 16x16 half %d\n", h); ++fail; }
         }
     }
+    // Epilogue strips of 2-byte outputs (strip_off, rows of 16, 8 or 4
+    // chunks): a one-to-one map onto the strip, and the writes -- 16x16
+    // blocks (lane l: row 16 h + l % 16, chunk epi16_chunk(pb, l / 16)),
+    // 32x32 blocks (row l % 32, chunk epi32_chunk(fn, j, l / 32)) -- and the
+    // row-contiguous read-back conflict-free.  The write model is pinned to
+    // the measured counts: lanes i, j of one clock on the same slot 1 extra
+    // clock, of different clocks 0; the 32x32 write under the XOR-by-line
+    // layout 8 extra clocks for 128- and 64-byte rows, 0 for 256-byte rows.
+    {
+        int epi_fail = 0;
+        for (int cprs : {16, 8, 4}) {
+            bool used[32 * 16] = {false};
+            for (int row = 0; row < 32; ++row)
+                for (int c = 0; c < cprs; ++c) {
+                    const int o = strip_off(cprs, row, c);
+                    if (o % 16 != 0 || o < 0 || o >= 32 * cprs * 16 || used[o / 16]) ++epi_fail;
+                    else used[o / 16] = true;
+                }
+            int offs[64];
+            for (int fn = 0; fn < cprs / 4; ++fn)
+                for (int j = 0; j < 2; ++j) {
+                    for (int l = 0; l < 64; ++l) offs[l] = strip_off(cprs, l % 32, epi32_chunk(fn, j, l / 32));
+                    if (write_extra_clocks(offs) != 0) ++epi_fail;
+                }
+            if (cprs == 16)
+                for (int h = 0; h < 2; ++h)
+                    for (int pb = 0; pb < 4; ++pb) {
+                        for (int l = 0; l < 64; ++l) offs[l] = strip_off(cprs, 16 * h + l % 16, epi16_chunk(pb, l / 16));
+                        if (write_extra_clocks(offs) != 0) ++epi_fail;
+                    }
+            const int rows_per_read = 64 / cprs;
+            for (int i = 0; i < 32 / rows_per_read; ++i) {
+                for (int l = 0; l < 64; ++l) offs[l] = strip_off(cprs, rows_per_read * i + l / cprs, l % cprs);
+                if (extra_clocks(offs) != 0) ++epi_fail;
+            }
+            // the measured counts
+            for (int c0 = 0; c0 < cprs; c0 += 2) {
+                for (int l = 0; l < 64; ++l) {
+                    const int row = l % 32;
+                    offs[l] = row * cprs * 16 + ((c0 + l / 32) ^ (((row * cprs) >> 4) & (cprs - 1))) * 16;
+                }
+                if (write_extra_clocks(offs) != (cprs == 16 ? 0 : 8)) { std::printf("write model off: cprs %d\n", cprs); ++epi_fail; }
+            }
+        }
+        for (int i : {0, 4, 16, 32})
+            for (int j = 0; j < 64; ++j) {
+                if (j == i) continue;
+                int offs[64];
+                for (int l = 0; l < 64; ++l) offs[l] = -1;
+                offs[i] = 0;
+                offs[j] = 256;
+                if (write_extra_clocks(offs) != (j / 8 == i / 8 ? 1 : 0)) { std::printf("write pair model off: %d %d\n", i, j); ++epi_fail; }
+            }
+        std::printf("epilogue strips (2-byte outputs): %s\n", epi_fail ? "FAIL" : "one-to-one, writes and read-back conflict-free");
+        fail += epi_fail;
+    }
     // every instance the library builds fits the LDS budget
     for (int dt = 0; dt < 4; ++dt)
         for (int tc = 0; tc < TILE_COUNT; ++tc)
@@ -162,11 +247,10 @@ int main() {
                                 for (int g0 = 0; g0 < 64; g0 += 32) {
                                     int hits[64] = {0};
                                     for (int l = g0; l < g0 + 32; ++l) {
-                                        const int h = l / 32, g = l / 16, j = l % 16;
                                         const int nf = wn * wtn + fn * 32;
-                                        int k, n;
-                                        if (dt == DT_I8) { k = st * 32 + 16 * h + 8 * r + j / 2; n = nf + 16 * (g & 1) + 8 * (j & 1); }
-                                        else { k = st * 16 + 8 * h + 4 * r + j / 4; n = nf + 16 * (g & 1) + 4 * (j & 3); }
+                                        const int k = st * (dt == DT_I8 ? 32 : 16) + rr_rows_per_read(dt) * r +
+                                                      rr_lane_k(dt, false, l);
+                                        const int n = nf + rr_lane_n(dt, false, l);
                                         const int c = n * sz / kChunk, b = n * sz % kChunk;
                                         const int addr = k * rb + ((sw ? c ^ swz_rr(dt, rb, k) : c) * kChunk) + b;
                                         for (int w = 0; w < 2; ++w) {
@@ -194,10 +278,10 @@ int main() {
                             for (int g0 = 0; g0 < 64; g0 += 32) {
                                 int hits[64] = {0};
                                 for (int l = g0; l < g0 + 32; ++l) {
-                                    const int g = l / 16, j = l % 16, nf = wn * wtn + idx * 16;
-                                    int k, n;
-                                    if (dt == DT_I8) { k = st * 64 + 16 * g + 8 * r + j / 2; n = nf + 8 * (j & 1); }
-                                    else { k = st * 32 + 8 * g + 4 * r + j / 4; n = nf + 4 * (j & 3); }
+                                    const int nf = wn * wtn + idx * 16;
+                                    const int k = st * (dt == DT_I8 ? 64 : 32) + rr_rows_per_read(dt) * r +
+                                                  rr_lane_k(dt, true, l);
+                                    const int n = nf + rr_lane_n(dt, true, l);
                                     const int c = n * sz / kChunk, b = n * sz % kChunk;
                                     const int addr = k * rb + (c ^ swz_rr(dt, rb, k)) * kChunk + b;
                                     for (int w = 0; w < 2; ++w) {
@@ -210,6 +294,27 @@ int main() {
                         }
         }
     }
+    // The lane formulas give each fragment column its k values in MFMA
+    // order: the transposing read hands out lane i the piece of the lane
+    // that addressed row piece (e * per + i / (16 / per)), element i mod
+    // (16 / per)... (16-bit: out lane i, element e <- lane 4e + i/4, element
+    // i%4; 8-bit: lane 2e + i/8, element i%8, measured).  So output lane i of
+    // a 16-lane group receives column n of its addressing lanes at the k of
+    // lanes 4e + i/4 (2e + i/8): consecutive k, the same column for all e.
+    for (int dt = 0; dt < 3; ++dt)
+        for (int b16 = 0; b16 < 2; ++b16)
+            for (int l = 0; l < 64; ++l) {
+                const int g0 = l & ~15, i = l & 15, epl = dt == DT_I8 ? 8 : 4;   // elements per lane
+                for (int e = 0; e < epl; ++e) {
+                    const int src = g0 + (dt == DT_I8 ? 2 * e + i / 8 : 4 * e + i / 4);
+                    const int col = rr_lane_n(dt, b16, src) + (dt == DT_I8 ? i % 8 : i % 4);
+                    const int col0 = rr_lane_n(dt, b16, g0 + (dt == DT_I8 ? i / 8 : i / 4)) + (dt == DT_I8 ? i % 8 : i % 4);
+                    if (col != col0 || rr_lane_k(dt, b16, src) != rr_lane_k(dt, b16, g0 + (dt == DT_I8 ? i / 8 : i / 4)) + e) {
+                        std::printf("RR lane formulas: dt %d b16 %d lane %d element %d\n", dt, b16, l, e);
+                        ++rr_fail;
+                    }
+                }
+            }
     std::printf("RR transposing reads: swizzled %s, unswizzled worst %d-way\n", rr_fail ? "CONFLICTS" : "conflict-free", rr_raw);
     if (rr_raw == 1) ++rr_fail;
     fail += rr_fail;
