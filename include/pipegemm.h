@@ -144,6 +144,10 @@ typedef struct {
                                 layout, int8/fp16/bf16) or 32; both give the
                                 same bits */
     int64_t workspace_bytes; /* workspace gemm_run_splitk needs (0 when splits = 1) */
+    int32_t waves_k;         /* waves sharing each C block, each taking its own
+                                run of every K-tile's k-steps; their partial
+                                sums are added in LDS after the K loop (1: none) */
+    int32_t reserved;
 } gemm_config_info_t;
 
 /* Bind a handle to HIP device `device`.  Allocates host memory for the

@@ -46,7 +46,7 @@ class ConfigInfo(ctypes.Structure):
         "reg_sets", "tiles_in_flight", "lds_bytes", "loads_per_tile")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
         ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("mfma_block", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_int64)]
+        ("workspace_bytes", ctypes.c_int64), ("waves_k", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -132,6 +132,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     in.block_k = bk;
     in.waves_m = ts.wm;
     in.waves_n = ts.wn;
+    in.waves_k = ts.wk;
     in.threads = pg::threads(tc);
     in.lds_slots = pg::lds_slots(variant, stages);
     in.reg_sets = pg::reg_sets(variant, stages);

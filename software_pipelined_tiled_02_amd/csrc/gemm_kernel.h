@@ -173,8 +173,8 @@ __device__ __forceinline__ void block_sync() {
 template <int DT, int LAYOUT, int TC, int STAGES, int VARIANT>
 struct Gemm {
     static constexpr TileShape TS = tile_shape(TC);
-    static constexpr int BM = TS.bm, BN = TS.bn, WM = TS.wm, WN = TS.wn;
-    static constexpr int T = WM * WN * 64;
+    static constexpr int BM = TS.bm, BN = TS.bn, WM = TS.wm, WN = TS.wn, WK = TS.wk;
+    static constexpr int T = WM * WN * WK * 64;
     static constexpr int SZ = in_size(DT), OSZ = out_size(DT), EPC = epc(DT);
     static constexpr int CPR = cpr_k(TC, STAGES, VARIANT); // chunks per K-contiguous row
     static constexpr int BK = CPR * EPC;
@@ -185,7 +185,10 @@ struct Gemm {
     static constexpr bool B16 = mfma_block16(DT, LAYOUT, TC, STAGES, VARIANT);
     static constexpr int BS = B16 ? 16 : 32;                // MFMA block edge
     static constexpr int FM = WTM / BS, FN = WTN / BS;
-    static constexpr int KSTEPS = CPR / (B16 ? 4 : 2);      // chunks per MFMA step: 2 (32x32) or 4 (16x16)
+    // MFMA steps of a K-tile per wave (chunks per step: 2 for 32x32 blocks, 4
+    // for 16x16); with WK k groups, group g takes steps g KSTEPS .. +KSTEPS-1
+    // of the K-tile's CPR / 2.
+    static constexpr int KSTEPS = CPR / (B16 ? 4 : 2) / WK;
     static constexpr int LA = loads_a(DT, TC, STAGES, VARIANT), LB = loads_b(DT, TC, STAGES, VARIANT);
     static constexpr int LPT = LA + LB;
     static constexpr int A_BYTES = BM * CPR * kChunk;
@@ -207,6 +210,7 @@ struct Gemm {
     static_assert(LPT * (STAGES > 1 ? STAGES - 1 : 1) < 64, "vmcnt range");
     static_assert(KSTEPS >= 2, "at least two MFMA steps per K-tile");
     static_assert(!B16 || (FM == 8 && FN == 8 && KSTEPS == 2), "16x16 blocks: 8 x 8 per wave, two steps");
+    static_assert(WK == 1 || (!B16 && (CPR / 2) % WK == 0), "k groups: 32x32 blocks, whole steps per group");
 
     // ---- per-lane state --------------------------------------------------
     struct State {
@@ -222,7 +226,7 @@ struct Gemm {
         int nbody, rot;                // the other K-tiles; the one they start at
         int tbase, tail0;              // physical K-tile of body tile 0; of head tile 0
         uint32_t klast;                // K index the last physical K-tile starts at
-        int tid, wave, wm, wn;
+        int tid, wave, wm, wn, wk;   // wk: the wave's k group (WK > 1)
     };
 
     __device__ static __forceinline__ void lds_dma(const State& s, bool is_a, uint8_t PG_LDS* dst, uint32_t voff,
@@ -391,7 +395,7 @@ struct Gemm {
     __device__ static __forceinline__ i32x4 read_b_rr(const State& s, const uint8_t PG_LDS* bt, int fn, int st) {
         if constexpr (SZ == 4) {
             const int lane = s.tid & 63;
-            const int n = s.wn * WTN + fn * 32 + (lane & 31), k0 = (2 * st + (lane >> 5)) * EPC;
+            const int n = s.wn * WTN + fn * 32 + (lane & 31), k0 = (2 * (s.wk * KSTEPS + st) + (lane >> 5)) * EPC;
             i32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = *(const int PG_LDS*)(bt + ((k0 + e) * BN + n) * 4);
@@ -693,6 +697,52 @@ struct Gemm {
         step<true>(s, smem, f[1], f[0], (kt + 1) & 1, 0, acc, 0, HALF, kt + 1 + R, 0, regs[(i + 1) % R]);
     }
 
+    // WK > 1: add the k groups' partial accumulators into group 0.  Groups
+    // 1 .. WK-1 store theirs in LDS (block, quarter, lane order, so 8
+    // consecutive lanes write 128 contiguous bytes: no bank conflict), and
+    // group 0 adds them in group order.  The ring is free: every wave's
+    // loads into LDS have completed (direct variant) and the barrier drains
+    // its LDS reads.
+    __device__ static __forceinline__ void add_k_groups(const State& s, uint8_t PG_LDS* smem, acc_t (&acc)[FM][FN]) {
+        constexpr int WB = FM * FN * 4 * 64 * 16;       // bytes per wave
+        static_assert((WK - 1) * WM * WN * WB <= LDS, "k-group sums fit the LDS");
+        const int lane = s.tid & 63, wmn = s.wave % (WM * WN);
+        block_sync();
+        if (s.wk > 0) {
+            uint8_t PG_LDS* base = smem + ((s.wk - 1) * WM * WN + wmn) * WB;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(i32x4 PG_LDS*)(base + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16) = out4_32(acc[fm][fn], q);
+        }
+        block_sync();
+        if (s.wk == 0) {
+#pragma unroll
+            for (int g = 1; g < WK; ++g) {
+                const uint8_t PG_LDS* base = smem + ((g - 1) * WM * WN + wmn) * WB;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const i32x4 v = *(const i32x4 PG_LDS*)(base + (((fm * FN + fn) * 4 + q) * 64 + lane) * 16);
+                            const f32x4 vf = __builtin_bit_cast(f32x4, v);   // whole vector, then index
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (DT == DT_I8)
+                                    acc[fm][fn][4 * q + e] += v[e];
+                                else
+                                    acc[fm][fn][4 * q + e] += vf[e];
+                            }
+                        }
+            }
+        }
+    }
+
     // Each workgroup computes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
     // (one tile when the grid covers C; several when the host launches one
     // workgroup per CU, so that a tile's C stores overlap the next tile's
@@ -721,8 +771,11 @@ struct Gemm {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(tp, 0, 0x7fffffff, kRsrcWord3);
         // 1. Lane (t, h) holds row t, columns 8q + 4h .. +3 of each 32x32 block
         //    (per-lane offset in the vector operand, the block's in the scalar
-        //    one); 16x16 blocks likewise.
-        if constexpr (B16) {
+        //    one); 16x16 blocks likewise.  With k groups, group 0 holds the
+        //    sums.
+        if (WK > 1 && s.wk != 0) {
+            // no partial of its own
+        } else if constexpr (B16) {
             // 16x16 blocks: lane l holds row (l % 16), columns 4 (l / 16) .. +3
             const int lane = s.tid & 63;
             const uint32_t vo = (uint32_t)(((s.wm * WTM + (lane & 15)) * BN + s.wn * WTN + 4 * (lane >> 4)) * 4);
@@ -802,7 +855,8 @@ struct Gemm {
         State s;
         s.tid = threadIdx.x;
         s.wave = __builtin_amdgcn_readfirstlane(s.tid >> 6);
-        s.wm = s.wave / WN;
+        s.wk = s.wave / (WM * WN);
+        s.wm = (s.wave % (WM * WN)) / WN;
         s.wn = s.wave % WN;
         const int lane = s.tid & 63;
 
@@ -893,7 +947,10 @@ struct Gemm {
                     const int k = rr_lane_k(DT, B16, lane);
                     const int n = s.wn * WTN + fn * BS + rr_lane_n(DT, B16, lane);
                     const int c = n * SZ / kChunk, b = n * SZ % kChunk;
-                    s.rrb[fn] = (uint32_t)(k * RB_RR + (c ^ swz_rr(DT, RB_RR, k)) * kChunk + b);
+                    // (the k group's first step: its k rows start 2 EPC per step on,
+                    // a whole number of swizzle periods)
+                    s.rrb[fn] = (uint32_t)(k * RB_RR + (c ^ swz_rr(DT, RB_RR, k)) * kChunk + b) +
+                                (uint32_t)(s.wk * KSTEPS * 2 * EPC * RB_RR);
                 }
             }
         } else {
@@ -919,7 +976,7 @@ struct Gemm {
                     s.rd16[st][half] = (uint32_t)(row * CPR + (c ^ swz(CPR, row))) * kChunk;
                 }
             } else {
-                s.rd[st] = (uint32_t)(t * CPR + ((2 * st + h) ^ swz(CPR, t))) * kChunk;
+                s.rd[st] = (uint32_t)(t * CPR + ((2 * (s.wk * KSTEPS + st) + h) ^ swz(CPR, t))) * kChunk;
             }
         }
 
@@ -1053,6 +1110,7 @@ struct Gemm {
             }
         }
 
+        if constexpr (WK > 1) add_k_groups(s, smem, acc);
         if (args.splits > 1) {
             splitk(args, smem, s, acc, p, m0, n0);
             return;
@@ -1072,6 +1130,7 @@ struct Gemm {
         // written with one 16-byte LDS write at strip_off (8-byte writes
         // measured bank conflicts in every layout).
         block_sync();
+        if (WK > 1 && s.wk != 0) return;   // group 0 holds the sums; no barrier follows
         const int t = lane & 31, h = lane >> 5;
         const int mw = m0 + s.wm * WTM, nw = n0 + s.wn * WTN;
         uint8_t PG_LDS* strip = smem + s.wave * STRIP_BYTES;

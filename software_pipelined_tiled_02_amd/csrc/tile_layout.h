@@ -44,6 +44,7 @@ enum Variant : int { VAR_REG = 0, VAR_DIRECT = 1, VAR_REG_KTAIL = 2 };
 enum TileClass : int { TILE_L = 0, TILE_M = 1, TILE_T = 2, TILE_W = 3, TILE_COUNT = 4 };
 
 constexpr int kMaxStages = 4;
+
 constexpr int kLdsBudget = 160 * 1024;   // bytes of LDS per CU on gfx950
 constexpr int kChunk = 16;               // bytes per lane per load
 
@@ -56,12 +57,19 @@ constexpr int epc(int dt) { return kChunk / in_size(dt); }
 // (bm/wm) x (bn/wn) block of C made of 32x32 MFMA blocks.  TILE_W is the
 // 256x256 tile with 8 waves (2 per SIMD, 128x64 each): while one wave of a
 // SIMD waits (on its loads, on the barrier), the other can issue MFMAs.
-struct TileShape { int bm, bn, wm, wn; };
+// wk > 1 splits each K-tile's k-steps over wk waves per C block (wave k
+// group g takes the g-th run of steps); after the K loop the groups' partial
+// accumulators are added through LDS.  The 32x64 tile runs two k groups:
+// its 2 x 1 waves of 32x32 left two of a CU's four SIMDs idle, and with the
+// K-tile's steps split over four waves each wave issues half the MFMAs and
+// fragment reads and a quarter of the loads (measured: fp32 256^3 7.5 ->
+// 5.9 us; the skinny bf16 shape's register-staged pairs 35-38 -> 32 us).
+struct TileShape { int bm, bn, wm, wn, wk; };
 constexpr TileShape tile_shape(int tc) {
-    return tc == TILE_L ? TileShape{256, 256, 2, 2}
-         : tc == TILE_W ? TileShape{256, 256, 2, 4}
-         : tc == TILE_M ? TileShape{128, 128, 2, 2}
-                        : TileShape{32, 64, 1, 2};
+    return tc == TILE_L ? TileShape{256, 256, 2, 2, 1}
+         : tc == TILE_W ? TileShape{256, 256, 2, 4, 1}
+         : tc == TILE_M ? TileShape{128, 128, 2, 2, 1}
+                        : TileShape{32, 64, 1, 2, 2};
 }
 
 // The 3-stage direct-to-LDS ring of the 256x256 classes is split by
@@ -125,11 +133,18 @@ constexpr int strip_row_bytes(int dt, int tc) {
 constexpr int epilogue_bytes(int dt, int tc) {
     return 32 * strip_row_bytes(dt, tc) * tile_shape(tc).wm * tile_shape(tc).wn;
 }
-constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
-    return ring_bytes(dt, tc, stages, variant) > epilogue_bytes(dt, tc) ? ring_bytes(dt, tc, stages, variant)
-                                                                        : epilogue_bytes(dt, tc);
+constexpr int threads(int tc) { return tile_shape(tc).wm * tile_shape(tc).wn * tile_shape(tc).wk * 64; }
+// LDS for adding the k groups' partial accumulators (wk > 1): the groups
+// g >= 1 each store their 32x32-block accumulators (16 words per lane and
+// block) for the group-0 waves to add.
+constexpr int kred_bytes(int tc) {
+    return (tile_shape(tc).wk - 1) * tile_shape(tc).wm * tile_shape(tc).wn *
+           (tile_shape(tc).bm / tile_shape(tc).wm / 32) * (tile_shape(tc).bn / tile_shape(tc).wn / 32) * 64 * 64;
 }
-constexpr int threads(int tc) { return tile_shape(tc).wm * tile_shape(tc).wn * 64; }
+constexpr int max3(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+constexpr int lds_bytes(int dt, int tc, int stages, int variant) {
+    return max3(ring_bytes(dt, tc, stages, variant), epilogue_bytes(dt, tc), kred_bytes(tc));
+}
 
 // 16-byte loads per lane per K-tile for each operand.
 constexpr int loads_a(int dt, int tc, int stages, int variant) {
