@@ -594,15 +594,22 @@ struct Gemm {
     // 0-3 already in f), reading the rest and the next step's (nslot, nst)
     // A/B 0-3 as above; loads of chunks [J0, J1) of K-tile ld_kt.  BAR: the
     // hand-over to the next K-tile -- wait for its data and cross the barrier
-    // after the first quadrant, once this step's own reads of its slot have
-    // completed (the barrier frees the slot for the loads that follow), and
-    // issue the loads after it.
+    // after the first (split ring) or second quadrant, once this step's own
+    // reads of its slot have completed (the barrier frees the slot for the
+    // loads that follow), and issue the loads after it.
     template <bool BAR, int WAITN>
     __device__ static __forceinline__ void step16(const State& s, uint8_t PG_LDS* smem, Frags& f, int cslot,
                                                   int cst, int nslot, int nst, acc_t (&acc)[FM][FN], int J0,
                                                   int J1, int ld_kt, int ld_slot, i32x4 (&regs)[LPT]) {
         const int NL = J1 - J0;
-        constexpr int LU0 = BAR ? 16 : 0;            // loads go in units [LU0, 64)
+        // The hand-over's wait and barrier: after the first quadrant in the
+        // split ring, after the second otherwise (the 2-stage ring's wait for
+        // the next tile then comes 16 MFMAs later; measured 3-6% faster at
+        // 2 stages, no change in the split ring).  Either way this step's own
+        // reads of its slot (first quadrant) are done and the next step's
+        // reads (third and fourth) come after it.
+        constexpr int BAR_U = SPLIT ? 15 : 31;
+        constexpr int LU0 = BAR ? BAR_U + 1 : 0;     // loads go in units [LU0, 64)
         uint32_t ld_sa = 0, ld_sb = 0;
 #pragma unroll
         for (int u = 0; u < 64; ++u) {
@@ -634,7 +641,7 @@ struct Gemm {
                     load_one(s, smem, ld_kt, ld_sa, ld_sb, ld_slot, regs, j);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (BAR && u == 15) {
+            if (BAR && u == BAR_U) {
                 wait_vmcnt<WAITN>();
                 block_sync();
                 __builtin_amdgcn_sched_barrier(0);
