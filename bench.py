@@ -68,6 +68,15 @@ WORKLOADS = {
     "bf16_1024x8192x8200": (1024, 8192, 8200, "bf16", "RC", "uniform", 1.0, "mfma",
                             "bf16 GEMM M=1024 N=8192 K=8200 (one GPU's share of M=N=8192 K=8200 "
                             "split 8 ways along M), fp32 accumulate, bf16 out"),
+    # partial last waves (tiles of 256x256 not a whole number of rounds of 256 CUs)
+    "bf16_5120x5120x5128": (5120, 5120, 5128, "bf16", "RC", "uniform", 1.0, "mfma",
+                            "bf16 GEMM M=N=5120 K=5128 (400 tiles of 256x256: 1.56 rounds), fp32 "
+                            "accumulate, bf16 out"),
+    "int8_4608x4608x4096": (4608, 4608, 4096, "i8", "RC", "int", 1.0, "mfma",
+                            "int8 IGEMM M=N=4608 K=4096 (324 tiles of 256x256: 1.27 rounds), int32 out"),
+    "bf16_4352x4352x4096": (4352, 4352, 4096, "bf16", "RC", "uniform", 1.0, "mfma",
+                            "bf16 GEMM M=N=4352 K=4096 (289 tiles of 256x256: 1.13 rounds), fp32 "
+                            "accumulate, bf16 out"),
 }
 # The five benchmark workloads, in the order they are measured; the first
 # MFMA-bound 4096^3 one (int8) is the headline.
@@ -259,15 +268,21 @@ def measure_workload(name, args, g, ceilings, res_table, pairs):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    if args.splits != 1:
-        # the split-K workspace, allocated (zeroed) once, before anything is timed
+    if args.splits != 1 or args.streamk:
+        # the split-K / stream-K workspace, allocated (zeroed) once, before anything is timed
         for s, v in pairs:
-            _, qi = binding.gemm_query(M, N, K, dtype, layout, s, v, tile=args.tile, splits=args.splits)
+            if args.streamk:
+                _, qi = binding.gemm_query_streamk(M, N, K, dtype, layout, s, v, grid=args.sk_grid, tile=args.tile)
+            else:
+                _, qi = binding.gemm_query(M, N, K, dtype, layout, s, v, tile=args.tile, splits=args.splits)
             g.workspace(qi["workspace_bytes"])
-    ws = g.workspace(1) if args.splits != 1 else None
+    ws = g.workspace(1) if (args.splits != 1 or args.streamk) else None
 
     def run_one(aa, bb, cc, s, v):
-        if args.splits == 1:
+        if args.streamk:
+            binding.gemm_run_streamk(g.h, M, N, K, dtype, layout, s, v, args.sk_grid, aa, K, bb, ldb, cc, N,
+                                     ws, ws.numel(), sh)
+        elif args.splits == 1:
             binding.gemm_run(g.h, M, N, K, dtype, layout, s, v, aa, K, bb, ldb, cc, N, sh)
         else:
             binding.gemm_run_splitk(g.h, M, N, K, dtype, layout, s, v, args.splits, aa, K, bb, ldb, cc, N,
@@ -335,7 +350,10 @@ def measure_workload(name, args, g, ceilings, res_table, pairs):
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)       # ms per launch
-        _, qi = binding.gemm_query(M, N, K, dtype, layout, s, v, tile=args.tile, splits=args.splits)
+        if args.streamk:
+            _, qi = binding.gemm_query_streamk(M, N, K, dtype, layout, s, v, grid=args.sk_grid, tile=args.tile)
+        else:
+            _, qi = binding.gemm_query(M, N, K, dtype, layout, s, v, tile=args.tile, splits=args.splits)
         results[(s, v)] = {
             "mean_us": round(mean * 1e3, 2), "median_us": round(per[len(per) // 2] * 1e3, 2),
             "min_us": round(per[0] * 1e3, 2), "max_us": round(per[-1] * 1e3, 2),
@@ -402,7 +420,8 @@ def measure_workload(name, args, g, ceilings, res_table, pairs):
         "value": round(value, 2), "unit": vunit, "best": pair_key(*best), "ms_per_step": round(r["ms_per_step"], 5),
         "tile": "%dx%dx%d" % (info["block_m"], info["block_n"], info["block_k"]),
         "lds_bytes": info["lds_bytes"], "grid": info["grid"], "splits": info["splits"],
-        "mfma_block": info["mfma_block"], "roofline": roof, "pairs_bit_identical": identical,
+        "sk_tiles": info["sk_tiles"], "mfma_block": info["mfma_block"], "roofline": roof,
+        "pairs_bit_identical": identical,
         "data": "synthetic (seeded), inputs resident in HBM, rotated over %d sets (%.0f MiB)" % (
             nrot, nrot * set_bytes / 2 ** 20),
         "pairs": {pair_key(*p): pair_record(q) for p, q in results.items()},
@@ -426,6 +445,9 @@ def main():
     ap.add_argument("--tile", default="auto", help="tile class: auto, 256x256, 256x256w8, 128x128, 32x64")
     ap.add_argument("--splits", type=int, default=1,
                     help="K splits per C tile (gemm_run_splitk); 0 = the library's choice")
+    ap.add_argument("--streamk", action="store_true", help="time gemm_run_streamk instead of gemm_run")
+    ap.add_argument("--sk-grid", type=int, default=0,
+                    help="stream-K workgroups (gemm_run_streamk's grid; 0 = one per CU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling-probe", action="store_true",
                     help="take the ceilings from profiles/ceilings.txt instead of measuring them")
@@ -491,7 +513,7 @@ def main():
         "config": {"workload": head["workload"], "M": M, "N": N, "K": K, "layout": head["layout"],
                    "stages": int(best_s), "variant": best_v, "tile": head["tile"],
                    "lds_bytes": head["lds_bytes"], "grid": head["grid"], "splits": head["splits"],
-                   "mfma_block": head["mfma_block"]},
+                   "sk_tiles": head["sk_tiles"], "mfma_block": head["mfma_block"]},
         "roofline": head["roofline"],
         "pairs_bit_identical": all(c["pairs_bit_identical"] for c in configs.values()),
         "rounds": args.rounds,

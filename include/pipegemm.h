@@ -68,10 +68,11 @@
  *
  * Errors.  Every entry point returns GEMM_OK (0) or one of the codes below;
  * nothing is thrown across the ABI.  Argument checks run before any HIP call,
- * so a rejected call has no side effect.  gemm_run, gemm_run_splitk and
- * gemm_run_splitk_noalloc are asynchronous: each enqueues one kernel launch on `stream` (and nothing
- * else, so a graph can capture it) and returns; faults during execution
- * surface at the caller's next synchronisation of that stream.
+ * so a rejected call has no side effect.  gemm_run, gemm_run_splitk,
+ * gemm_run_streamk and gemm_run_splitk_noalloc are asynchronous: each
+ * enqueues one kernel launch on `stream` (and nothing else, so a graph can
+ * capture it) and returns; faults during execution surface at the caller's
+ * next synchronisation of that stream.
  */
 #ifndef PIPEGEMM_H
 #define PIPEGEMM_H
@@ -143,11 +144,14 @@ typedef struct {
                                 (4-wave 256x256 tile, 2-3 direct stages, either
                                 layout, int8/fp16/bf16) or 32; both give the
                                 same bits */
-    int64_t workspace_bytes; /* workspace gemm_run_splitk needs (0 when splits = 1) */
+    int64_t workspace_bytes; /* workspace gemm_run_splitk needs (0 when splits = 1),
+                                or gemm_run_streamk (see there) */
     int32_t waves_k;         /* waves sharing each C block, each taking its own
                                 run of every K-tile's k-steps; their partial
                                 sums are added in LDS after the K loop (1: none) */
-    int32_t reserved;
+    int32_t sk_tiles;        /* gemm_run_streamk: C tiles shared out stream-K
+                                (the last sk_tiles of the c_tiles); the others
+                                run data-parallel.  0 otherwise */
 } gemm_config_info_t;
 
 /* Bind a handle to HIP device `device`.  Allocates host memory for the
@@ -205,6 +209,44 @@ int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
                     void *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
                     void *stream);
 
+/* C = A * B with the tiles shared out stream-K over `grid` workgroups
+ * (0: one per compute unit), for shapes whose C tiles do not fill a whole
+ * number of rounds of the grid (a partial last wave: e.g. 400 tiles of
+ * 256 x 256 on 256 CUs take two rounds of gemm_run, the second 56% full).
+ * This is the other half of the split-K / stream-K pair "CUDA Kernel Study:
+ * Pipelining" (Detailed Analysis) and "Part 4 -- Pipelining and Occupancy"
+ * (gpucourse.com, section 4.2: occupancy and waves of blocks) point to.
+ *   Every full round of `grid` tiles but the last runs as in gemm_run (one
+ *   tile per workgroup at a time).  The remaining sk_tiles tiles (between
+ *   one and two rounds' worth, or all of them when there are fewer than two
+ *   rounds) are cut into units of the tile class's largest K-tile, numbered
+ *   tile by tile, and workgroup g takes the g-th of `grid` equal runs of
+ *   units (sizes differ by at most one).  A tile covered by one workgroup is
+ *   stored as in gemm_run; a tile split between several is summed from
+ *   their fp32 (int32 for GEMM_I8) partial tiles by whichever arrives last,
+ *   in K order, so the result does not depend on arrival order, every
+ *   (stages, variant) pair returns bit-identical C for a given grid, and
+ *   int8 stays exact.  Float results may differ from gemm_run's in the last
+ *   bits (the partial sums are grouped differently).
+ *   The grid used is min(grid, sk_tiles x units); gemm_query_streamk
+ *   reports it, sk_tiles and the workspace size.
+ * Workspace: caller-owned device memory of at least info.workspace_bytes =
+ *   65536 + 2 x grid x block_m x block_n x 4 bytes, 256-byte aligned,
+ *   overlapping none of A, B, C; its first 65536 bytes are arrival counters
+ *   that must be zero before the first use and are zero again after every
+ *   completed call (as for gemm_run_splitk, whose workspace it may share).
+ *   Calls that share a workspace must not run concurrently.  NULL / 0 is
+ *   accepted when sk_tiles is 0 (M or N = 0).
+ * Errors: as gemm_run; also GEMM_ERR_INVALID_ARG for grid < 0 or a NULL or
+ * too small workspace, GEMM_ERR_ALIGNMENT for a workspace not 256-byte
+ * aligned, GEMM_ERR_UNSUPPORTED for more than 16384 C tiles or a grid whose
+ * partial tiles would pass 2 GiB. */
+int gemm_run_streamk(gemm_handle_t h, int64_t M, int64_t N, int64_t K,
+                     int dtype, int layout, int stages, int variant, int grid,
+                     const void *A, int64_t lda, const void *B, int64_t ldb,
+                     void *C, int64_t ldc, void *workspace, int64_t workspace_bytes,
+                     void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * gemm_run_splitk with the library's own static scratch buffer as its
@@ -249,6 +291,13 @@ int gemm_query_splitk(int64_t M, int64_t N, int64_t K, int dtype, int layout, in
                       int variant, int tile, int splits, const void *A, int64_t lda,
                       const void *B, int64_t ldb, const void *C, int64_t ldc,
                       gemm_config_info_t *info);
+
+/* gemm_query for gemm_run_streamk: the tile, grid, sk_tiles and workspace
+ * size that call would use (for a 256-CU device when grid = 0). */
+int gemm_query_streamk(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+                       int variant, int tile, int grid, const void *A, int64_t lda,
+                       const void *B, int64_t ldb, const void *C, int64_t ldc,
+                       gemm_config_info_t *info);
 
 /* Resources and occupancy of the kernel instance gemm_run would launch for a
  * call (see gemm_occupancy), the figures the "Part 4 -- Pipelining and

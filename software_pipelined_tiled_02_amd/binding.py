@@ -28,7 +28,7 @@ TILES = {"auto": GEMM_TILE_AUTO, "256x256": GEMM_TILE_256x256, "128x128": GEMM_T
 # C functions exported by the library (the names include/pipegemm.h declares)
 EXPORTS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_set_tile", "gemm_query",
            "gemm_run_splitk", "gemm_query_splitk", "gemm_status_string", "gemm_last_hip_error",
-           "gemm_run_splitk_noalloc", "gemm_occupancy")
+           "gemm_run_splitk_noalloc", "gemm_occupancy", "gemm_run_streamk", "gemm_query_streamk")
 
 
 class GemmError(RuntimeError):
@@ -46,7 +46,7 @@ class ConfigInfo(ctypes.Structure):
         "reg_sets", "tiles_in_flight", "lds_bytes", "loads_per_tile")] + [
         ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int32),
         ("c_tiles", ctypes.c_int32), ("splits", ctypes.c_int32), ("mfma_block", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_int64), ("waves_k", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        ("workspace_bytes", ctypes.c_int64), ("waves_k", ctypes.c_int32), ("sk_tiles", ctypes.c_int32)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -84,6 +84,12 @@ def _lib():
         lib.gemm_run_splitk.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
                                         vp, i64, vp]
         lib.gemm_run_splitk.restype = ci
+        lib.gemm_run_streamk.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
+                                         vp, i64, vp]
+        lib.gemm_run_streamk.restype = ci
+        lib.gemm_query_streamk.argtypes = [i64, i64, i64, ci, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp, i64,
+                                           ctypes.POINTER(ConfigInfo)]
+        lib.gemm_query_streamk.restype = ci
         lib.gemm_run_splitk_noalloc.argtypes = [vp, i64, i64, i64, ci, ci, ci, ci, ci, vp, i64, vp, i64, vp,
                                                 i64, vp]
         lib.gemm_run_splitk_noalloc.restype = ci
@@ -168,6 +174,18 @@ def gemm_run_splitk(h, M, N, K, dtype, layout, stages, variant, splits, A, lda, 
     return rc
 
 
+def gemm_run_streamk(h, M, N, K, dtype, layout, stages, variant, grid, A, lda, B, ldb, C, ldc,
+                     workspace, workspace_bytes, stream=None, check=True):
+    """Enqueue C = A * B with the tiles shared out stream-K over `grid`
+    workgroups (0: one per compute unit)."""
+    rc = _lib().gemm_run_streamk(h, M, N, K, _enum(dtype, DTYPES), _enum(layout, LAYOUTS), int(stages),
+                                 _enum(variant, VARIANTS), int(grid), _ptr(A), lda, _ptr(B), ldb,
+                                 _ptr(C), ldc, _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_run_streamk")
+    return rc
+
+
 def gemm_run_splitk_noalloc(h, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb, C, ldc,
                             stream=None, check=True):
     """Enqueue C = A * B with K split over `splits` workgroups per C tile,
@@ -207,6 +225,23 @@ def gemm_query(M, N, K, dtype, layout, stages, variant, tile="auto", A=0, lda=No
     return rc, info.as_dict()
 
 
+def gemm_query_streamk(M, N, K, dtype, layout, stages, variant, grid=0, tile="auto", A=0, lda=None, B=0,
+                       ldb=None, C=0, ldc=None, check=True):
+    """The configuration gemm_run_streamk would use (no HIP call).  Returns
+    (status, dict)."""
+    layout_v = _enum(layout, LAYOUTS)
+    lda = K if lda is None else lda
+    ldb = (N if layout_v == GEMM_LAYOUT_RR else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    info = ConfigInfo()
+    rc = _lib().gemm_query_streamk(M, N, K, _enum(dtype, DTYPES), layout_v, int(stages),
+                                   _enum(variant, VARIANTS), _enum(tile, TILES), int(grid), A, lda, B,
+                                   ldb, C, ldc, ctypes.byref(info))
+    if check and rc != GEMM_OK:
+        raise GemmError(rc, "gemm_query_streamk")
+    return rc, info.as_dict()
+
+
 class Gemm:
     """Owns a handle; ``run`` takes torch CUDA tensors in the ABI's storage:
     A (M x K row-major), B (K x N row-major for RR, its N x K transpose for
@@ -219,7 +254,8 @@ class Gemm:
         self._ws = None   # split-K workspace: zeroed once, left zeroed by every call
 
     def workspace(self, nbytes):
-        """A device buffer of at least nbytes for gemm_run_splitk (grown, zeroed, on demand)."""
+        """A device buffer of at least nbytes for gemm_run_splitk / gemm_run_streamk (grown,
+        zeroed, on demand)."""
         import torch
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device="cuda:%d" % self.device)
@@ -260,3 +296,12 @@ class Gemm:
         ws = self.workspace(info["workspace_bytes"]) if info["workspace_bytes"] > 0 else None
         return gemm_run_splitk(self.h, M, N, K, dtype, layout, stages, variant, splits, A, lda, B, ldb,
                                C, ldc, ws, ws.numel() if ws is not None else 0, stream, check)
+
+    def run_streamk(self, M, N, K, dtype, layout, stages, variant, grid, A, lda, B, ldb, C, ldc,
+                    stream=None, check=True):
+        """gemm_run_streamk with this handle's tile and workspace."""
+        _, info = gemm_query_streamk(M, N, K, dtype, layout, stages, variant, grid=grid, tile=self.tile,
+                                     lda=lda, ldb=ldb, ldc=ldc, check=False)
+        ws = self.workspace(info["workspace_bytes"]) if info["workspace_bytes"] > 0 else None
+        return gemm_run_streamk(self.h, M, N, K, dtype, layout, stages, variant, grid, A, lda, B, ldb, C, ldc,
+                                ws, 0 if ws is None else ws.numel(), stream, check)

@@ -60,16 +60,18 @@ bool instance_exists(int layout, int tile) {
 }
 
 // Every check of the ABI, then the configuration.  No HIP call.
+// sk_grid: -1 for a call without stream-K; otherwise the stream-K grid (0:
+// one workgroup per CU).
 int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
-              int tile, int splits, const void* A, int64_t lda, const void* B, int64_t ldb, const void* C,
-              int64_t ldc, int num_cus, bool query, Plan* plan) {
+              int tile, int splits, int sk_grid, const void* A, int64_t lda, const void* B, int64_t ldb,
+              const void* C, int64_t ldc, int num_cus, bool query, Plan* plan) {
     if (dtype < GEMM_I8 || dtype > GEMM_F32) return GEMM_ERR_INVALID_ARG;
     if (layout != GEMM_LAYOUT_RR && layout != GEMM_LAYOUT_RC) return GEMM_ERR_INVALID_ARG;
     if (variant != GEMM_VARIANT_REG && variant != GEMM_VARIANT_DIRECT) return GEMM_ERR_INVALID_ARG;
     if (stages < 1 || stages > pg::kMaxStages) return GEMM_ERR_INVALID_ARG;
     if (tile < GEMM_TILE_AUTO || tile >= pg::TILE_COUNT) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_ARG;
-    if (splits < 0) return GEMM_ERR_INVALID_ARG;
+    if (splits < 0 || sk_grid < -1 || (sk_grid >= 0 && splits > 1)) return GEMM_ERR_INVALID_ARG;
 
     const bool has_c = M > 0 && N > 0;
     const bool reads_a = M > 0 && K > 0 && N > 0;
@@ -162,12 +164,28 @@ int plan_call(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages
     if (P > units) P = units;
     if (P > kMaxSplits) P = kMaxSplits;
     if (P < 1) P = 1;
+    if (sk_grid >= 0) P = 1;
     if (P > 1 && tm * tn > pg::kSplitkCounters) return GEMM_ERR_UNSUPPORTED;
     in.splits = (int32_t)P;
     in.workspace_bytes = P > 1 ? splitk_workspace(tm * tn, P, ts) : 0;
     const int64_t work = tm * tn * P;
     if (work > INT_MAX) return GEMM_ERR_UNSUPPORTED;
     in.grid = ((tc == pg::TILE_L || tc == pg::TILE_W) && work > num_cus && num_cus % 8 == 0) ? num_cus : work;
+    if (sk_grid >= 0 && tm * tn > 0) {
+        // Stream-K: G workgroups; every full round of G tiles but the last
+        // is data-parallel, and the rest (between one and two rounds' worth)
+        // is shared out in units over all G workgroups, so each gets the
+        // same number of units, give or take one.
+        int64_t G = sk_grid > 0 ? sk_grid : num_cus;
+        const int64_t U = units > 0 ? units : 1, full = tm * tn / G;
+        const int64_t dp = full >= 2 ? (full - 1) * G : 0, sk = tm * tn - dp;
+        if (G > sk * U) G = sk * U;
+        if (tm * tn > pg::kSplitkCounters) return GEMM_ERR_UNSUPPORTED;
+        if (2 * G * (int64_t)ts.bm * ts.bn * 4 >= ((int64_t)1 << 31)) return GEMM_ERR_UNSUPPORTED;
+        in.sk_tiles = (int32_t)sk;
+        in.grid = G;
+        in.workspace_bytes = pg::kSplitkCounterBytes + 2 * G * (int64_t)ts.bm * ts.bn * 4;
+    }
     in.k_tiles = ceil_div(K, bk);
     in.k_tail = (int32_t)(K % bk);
     plan->tile = tc;
@@ -270,7 +288,8 @@ int launch(gemm_handle_t h, const Plan& plan, int64_t M, int64_t N, int64_t K, i
     args.tiles_m = (int32_t)plan.tiles_m;
     args.tiles_n = (int32_t)plan.tiles_n;
     args.splits = plan.info.splits;
-    args.ws = plan.info.splits > 1 ? ws : nullptr;
+    args.sk_tiles = plan.info.sk_tiles;
+    args.ws = (plan.info.splits > 1 || plan.info.sk_tiles > 0) ? ws : nullptr;
 
     int cur = -1;
     hipError_t e = hipGetDevice(&cur);
@@ -333,7 +352,18 @@ int gemm_query_splitk(int64_t M, int64_t N, int64_t K, int dtype, int layout, in
                       const void* C, int64_t ldc, gemm_config_info_t* info) {
     if (info == nullptr) return GEMM_ERR_INVALID_ARG;
     Plan plan;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, splits, A, lda, B, ldb, C, ldc,
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, splits, -1, A, lda, B, ldb, C, ldc,
+                       kDefaultCus, true, &plan);
+    if (rc == GEMM_OK) *info = plan.info;
+    return rc;
+}
+
+int gemm_query_streamk(int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages, int variant,
+                       int tile, int grid, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, int64_t ldc, gemm_config_info_t* info) {
+    if (info == nullptr || grid < 0) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, tile, 1, grid, A, lda, B, ldb, C, ldc,
                        kDefaultCus, true, &plan);
     if (rc == GEMM_OK) *info = plan.info;
     return rc;
@@ -350,10 +380,25 @@ int gemm_run_splitk(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype,
                     int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream) {
     if (h == nullptr || workspace_bytes < 0) return GEMM_ERR_INVALID_ARG;
     Plan plan;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, A, lda, B, ldb, C,
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, -1, A, lda, B, ldb, C,
                        ldc, h->num_cus, false, &plan);
     if (rc != GEMM_OK) return rc;
     if (plan.info.splits > 1) {
+        if (workspace == nullptr || workspace_bytes < plan.info.workspace_bytes) return GEMM_ERR_INVALID_ARG;
+        if (((uintptr_t)workspace & 255u) != 0) return GEMM_ERR_ALIGNMENT;
+    }
+    return launch(h, plan, M, N, K, dtype, layout, stages, A, lda, B, ldb, C, ldc, workspace, stream);
+}
+
+int gemm_run_streamk(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int layout, int stages,
+                     int variant, int grid, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                     int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (h == nullptr || workspace_bytes < 0 || grid < 0) return GEMM_ERR_INVALID_ARG;
+    Plan plan;
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, 1, grid, A, lda, B, ldb, C,
+                       ldc, h->num_cus, false, &plan);
+    if (rc != GEMM_OK) return rc;
+    if (plan.info.sk_tiles > 0) {
         if (workspace == nullptr || workspace_bytes < plan.info.workspace_bytes) return GEMM_ERR_INVALID_ARG;
         if (((uintptr_t)workspace & 255u) != 0) return GEMM_ERR_ALIGNMENT;
     }
@@ -365,7 +410,7 @@ int gemm_run_splitk_noalloc(gemm_handle_t h, int64_t M, int64_t N, int64_t K, in
                             int64_t ldb, void* C, int64_t ldc, void* stream) {
     if (h == nullptr) return GEMM_ERR_INVALID_ARG;
     Plan plan;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, A, lda, B, ldb, C,
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, splits, -1, A, lda, B, ldb, C,
                        ldc, h->num_cus, false, &plan);
     if (rc != GEMM_OK) return rc;
     if (plan.info.workspace_bytes > (int64_t)GEMM_NOALLOC_SCRATCH_BYTES) return GEMM_ERR_SCRATCH;
@@ -384,8 +429,8 @@ int gemm_occupancy(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, 
     if (h == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
     Plan plan;
     const int64_t ldb = layout == GEMM_LAYOUT_RR ? N : K;
-    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, 1, nullptr, K, nullptr, ldb,
-                       nullptr, N, h->num_cus, true, &plan);
+    int rc = plan_call(M, N, K, dtype, layout, stages, variant, h->tile_override, 1, -1, nullptr, K, nullptr,
+                       ldb, nullptr, N, h->num_cus, true, &plan);
     if (rc != GEMM_OK) return rc;
     const void* fn = registry().fn[dtype][layout][plan.tile][stages][plan.kernel_variant];
     if (fn == nullptr) return GEMM_ERR_UNSUPPORTED;

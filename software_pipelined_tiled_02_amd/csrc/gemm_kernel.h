@@ -750,32 +750,41 @@ struct Gemm {
         }
     }
 
-    // Each workgroup computes tiles blockIdx.x, blockIdx.x + gridDim.x, ...
-    // (one tile when the grid covers C; several when the host launches one
-    // workgroup per CU, so that a tile's C stores overlap the next tile's
-    // prologue loads).
-    // Split K: each split writes its accumulators to the workspace as a
-    // BM x BN tile of 4-byte words and counts itself in the tile's arrival
-    // counter.  The split that arrives last adds the partial tiles in split
-    // order 0, 1, ..., rounds once and stores C; the others are done.
-    // Nothing waits for another workgroup, and the sum's order does not
-    // depend on which split is last.  The last one puts the counter back to
-    // 0, so the counters are zero again after every call.
+    // Partial tiles (split K, stream-K).  Each contributor of a tile writes
+    // its accumulators to the workspace as a BM x BN tile of 4-byte words
+    // and counts itself in the tile's arrival counter.  The contributor that
+    // arrives last adds the partial tiles in K order, rounds once and
+    // stores C; the others are done.  Nothing waits for another workgroup,
+    // and the sum's order does not depend on which contributor is last.  The
+    // last one puts the counter back to 0, so the counters are zero again
+    // after every call.
+    //   Split K (mode 1): contributor p of `splits` writes slot p of the
+    // tile's own `splits` slots.  Stream-K (mode 2): the contributors of
+    // tile t are the workgroups sk_owner(first unit) .. sk_owner(last unit),
+    // each writing the slot sk_slot gives it (slot `part`).
     //   Visibility across XCDs (each has its own L2) without an L2-wide
     // write-back or invalidate: the partials are written and read with
     // device-scope stores and loads (the scope bits of the buffer
     // instructions: written through to memory, read from it), every store
     // has completed before the counter is incremented, and the partials are
     // read only after the increment that finds all the others.
-    //   workspace: kSplitkCounters uint32 counters, then
-    //   [ntiles][splits][BM][BN] accumulator words.
-    __device__ static __forceinline__ void splitk(const GemmArgs& args, uint8_t PG_LDS* smem, const State& s,
-                                                  const acc_t (&acc)[FM][FN], int p, int m0, int n0) {
+    //   workspace: kSplitkCounters uint32 counters, then the partial tiles:
+    //   split K [ntiles][splits][BM][BN], stream-K [2 x grid][BM][BN] words.
+    __device__ static __forceinline__ void partial(const GemmArgs& args, uint8_t PG_LDS* smem, const State& s,
+                                                   const acc_t (&acc)[FM][FN], int mode, int part, int j, int m0,
+                                                   int n0) {
         constexpr int PART = BM * BN * 4;
         const int tile = (m0 / BM) * args.tiles_n + n0 / BN;   // any one-to-one tile number will do
         uint32_t* cnt = (uint32_t*)args.ws;
-        uint8_t* tp = (uint8_t*)args.ws + kSplitkCounterBytes + (size_t)tile * args.splits * PART;
+        uint8_t* tp = (uint8_t*)args.ws + kSplitkCounterBytes + (mode == 1 ? (size_t)tile * args.splits * PART : 0);
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(tp, 0, 0x7fffffff, kRsrcWord3);
+        // Contributors of the tile, and the first one's stream-K numbers.
+        constexpr int BKMAX = block_k(DT, TC, 1, VARIANT);
+        const int64_t U = args.K / BKMAX > 0 ? args.K / BKMAX : 1, G = gridDim.x;
+        const int64_t total = (int64_t)args.sk_tiles * U;
+        const int64_t t0 = (int64_t)(j - (args.tiles_m * args.tiles_n - args.sk_tiles)) * U;
+        const int64_t g0 = mode == 2 ? sk_owner(t0, G, total) : 0;
+        const int nparts = mode == 2 ? (int)(sk_owner(t0 + U - 1, G, total) - g0 + 1) : args.splits;
         // 1. Lane (t, h) holds row t, columns 8q + 4h .. +3 of each 32x32 block
         //    (per-lane offset in the vector operand, the block's in the scalar
         //    one); 16x16 blocks likewise.  With k groups, group 0 holds the
@@ -786,7 +795,7 @@ struct Gemm {
             // 16x16 blocks: lane l holds row (l % 16), columns 4 (l / 16) .. +3
             const int lane = s.tid & 63;
             const uint32_t vo = (uint32_t)(((s.wm * WTM + (lane & 15)) * BN + s.wn * WTN + 4 * (lane >> 4)) * 4);
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)p * PART);
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)part * PART);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -796,7 +805,7 @@ struct Gemm {
         } else {
             const int lane = s.tid & 63, t = lane & 31, h = lane >> 5;
             const uint32_t vo = (uint32_t)(((s.wm * WTM + t) * BN + s.wn * WTN + 4 * h) * 4);
-            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)p * PART);
+            const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)part * PART);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -812,31 +821,50 @@ struct Gemm {
         if (s.tid == 0)                    // ... before it is counted
             *(volatile uint32_t PG_LDS*)smem =
                 __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (uint32_t)(args.splits - 1);
+                (uint32_t)(nparts - 1);
         block_sync();
         if (*(volatile uint32_t PG_LDS*)smem == 0) return;
-        // 2. Four consecutive columns per lane and chunk (a wave covers 256
-        //    contiguous words of the tile), each split's added in split
-        //    order.  (Batching chunks, U > 1, raised the register peak of
-        //    the whole kernel and cost waves per SIMD in some instances.)
-        constexpr int ITER = BM * BN / (4 * T), U = 1;
-        static_assert(ITER % U == 0, "split-K chunks");
-        for (int it0 = 0; it0 < ITER; it0 += U) {
-            i32x4 sum[U];
+        // 2. Four consecutive columns per lane and iteration (a wave covers
+        //    256 contiguous words of the tile per iteration), in chunks of CH
+        //    iterations: a contributor's CH loads of a chunk are in flight
+        //    together, and the next contributor's are issued before the
+        //    current one's are added, so a chunk costs about one memory
+        //    latency instead of one per iteration and contributor (summing
+        //    one 16-byte word at a time made the finisher of a 256x256 tile
+        //    latency-bound: 64 iterations x contributors round trips).
+        //    Contributors are added in K order.
+        //    Only the 4-wave 256x256 tile batches iterations (CH = 8): it
+        //    runs one wave per SIMD with registers to spare, while in the
+        //    other classes the chunk's 3 x CH x 4 registers raised the
+        //    kernel's register peak (fewer waves per SIMD, or spills in the
+        //    8-wave tile).
+        constexpr int ITER = BM * BN / (4 * T);
+        constexpr int CH = TC == TILE_L ? 8 : 1;
+        static_assert(ITER % CH == 0, "finisher chunks");
+        for (int it0 = 0; it0 < ITER; it0 += CH) {
+            i32x4 sum[CH], cur[CH], nxt[CH];
+            auto fetch = [&](i32x4 (&v)[CH], int q) {
+                const int slot = mode == 2 ? (int)sk_slot(g0 + q, t0, G, total) : q;
+                const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)slot * PART);
 #pragma unroll
-            for (int u = 0; u < U; ++u) sum[u] = i32x4{0, 0, 0, 0};
-            for (int q = 0; q < args.splits; ++q) {
-                i32x4 v[U];
+                for (int u = 0; u < CH; ++u)
+                    v[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(((it0 + u) * T + s.tid) * 16), so,
+                                                                 kScopeDevice);
+            };
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rw, (uint32_t)(((it0 + u) * T + s.tid) * 16), __builtin_amdgcn_readfirstlane((uint32_t)q * PART),
-                        kScopeDevice);
+            for (int u = 0; u < CH; ++u) sum[u] = i32x4{0, 0, 0, 0};
+            fetch(cur, 0);
+            for (int q = 0; q + 1 < nparts; ++q) {
+                fetch(nxt, q + 1);
 #pragma unroll
-                for (int u = 0; u < U; ++u) sum[u] = add_acc(sum[u], v[u]);
+                for (int u = 0; u < CH; ++u) {
+                    sum[u] = add_acc(sum[u], cur[u]);
+                    cur[u] = nxt[u];
+                }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < CH; ++u) {
+                sum[u] = add_acc(sum[u], cur[u]);
                 const int idx = ((it0 + u) * T + s.tid) * 4;
                 const int m = idx / BN, n = idx % BN;
                 if (m0 + m < args.M) store_out4(args, m0 + m, n0 + n, sum[u]);
@@ -845,20 +873,82 @@ struct Gemm {
         if (s.tid == 0) __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // With K split in `splits` parts, work item j is split j / ntiles of
-    // tile j % ntiles (consecutive workgroups share a K range).
+    // A workgroup's work: the data-parallel tiles blockIdx.x, blockIdx.x +
+    // gridDim.x, ... (with K split in `splits` parts, work item j is split
+    // j / ntiles of tile j % ntiles: consecutive workgroups share a K range);
+    // then, when the last sk_tiles tiles are shared out stream-K, its range
+    // of their units (sk_begin), one piece per tile it touches.
     __device__ static __forceinline__ void run(const GemmArgs args, uint8_t PG_LDS* smem) {
-        const int ntiles = args.tiles_m * args.tiles_n;
-        const int nwork = ntiles * args.splits;
-        for (int j = blockIdx.x; j < nwork; j += gridDim.x) {
-            if (j != (int)blockIdx.x) block_sync();   // every wave is done with the last strips
-            const int p = j / ntiles;
-            run_tile(args, smem, j - p * ntiles, ntiles, p);
+        constexpr int BKMAX = block_k(DT, TC, 1, VARIANT);
+        const int units = args.K / BKMAX;
+        const int ndp = args.tiles_m * args.tiles_n - args.sk_tiles;
+        const int nwork = ndp * args.splits;
+        const int64_t U = units > 0 ? units : 1;   // stream-K: a K below one unit is one unit, the head
+        const int64_t G = gridDim.x, total = (int64_t)args.sk_tiles * U;
+        // Stream-K calls number the workgroups XCD by XCD (workgroup b runs
+        // on XCD b mod 8), so that the workgroups of one XCD take
+        // consecutive data-parallel tiles and a consecutive run of units,
+        // and take the tiles in plain band order: the tiles an XCD works on
+        // at a time then share A rows and B columns in its L2, as the
+        // regrouping in run_tile arranges for the other calls.
+        const bool skm = args.sk_tiles > 0;
+        const int vb = (skm && (gridDim.x & 7) == 0) ? (int)((blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3))
+                                                     : (int)blockIdx.x;
+        const int64_t i0 = skm ? sk_begin(vb, G, total) : 0;
+        const int64_t e = skm ? sk_begin(vb + 1, G, total) : 0;
+        int64_t i = i0;
+        bool first = true;
+        // One call site of run_tile (it is inlined): each pass takes the
+        // next data-parallel item, else the next stream-K piece.
+        for (int j = vb;;) {
+            int tile, u0, u1, mode, part, rot_u = -1;
+            bool last;
+            if (j < nwork) {
+                const int p = j / ndp;
+                tile = j - p * ndp;
+                u0 = p * units / args.splits;
+                u1 = (p + 1) * units / args.splits;
+                last = p == args.splits - 1;
+                mode = args.splits > 1 ? 1 : 0;
+                part = p;
+                j += gridDim.x;
+            } else if (i < e) {
+                const int64_t t = i / U, a = i - t * U, b = sk_piece_end(i, e, U);
+                tile = ndp + (int)t;
+                u0 = (int)(a < units ? a : units);
+                u1 = (int)(b < units ? b : units);
+                last = b == U;
+                mode = (a == 0 && b == U) ? 0 : 2;
+                part = (int)(2 * vb + (i == i0 ? 0 : 1));
+                // Keep the workgroups of an XCD on one K unit at a time, as
+                // in the data-parallel rounds (unit 9x + step of XCD x; the
+                // workgroups of an XCD work on neighbouring tiles, which
+                // then share A rows and B columns in its L2 only if they
+                // read the same K columns together): start the piece at the
+                // unit that puts this workgroup's step i - i0 on that unit,
+                // or, when that unit lies outside the piece, at the unit
+                // that reaches it when it enters.
+                const int64_t len = b - a, d = (i - i0 + 9 * (int64_t)(blockIdx.x & 7) + U - a % U) % U;
+                rot_u = (int)((((d >= len ? d - U : d) % len) + len) % len);
+                i += b - a;
+            } else {
+                break;
+            }
+            if (!first) block_sync();   // every wave is done with the last strips
+            first = false;
+            run_tile(args, smem, tile, u0, u1, last, mode, part, skm, rot_u);
         }
     }
 
-    __device__ static __forceinline__ void run_tile(const GemmArgs args, uint8_t PG_LDS* smem, int j, int ntiles,
-                                                    int p) {
+    // Tile j, units [u0, u1) of its K loop (the ragged head too when
+    // `last`); mode 0 stores C, mode 1 writes split `part`'s partial tile,
+    // mode 2 stream-K partial slot `part` (summed by whichever contributor
+    // of the tile arrives last).  The K loop starts at unit u0 + rot_u
+    // (rot_u >= 0) or at the XCD's rotation (rot_u = -1).
+    __device__ static __forceinline__ void run_tile(const GemmArgs args, uint8_t PG_LDS* smem, int j, int u0,
+                                                    int u1, bool last, int mode, int part, bool band_order,
+                                                    int rot_u) {
+        const int ntiles = args.tiles_m * args.tiles_n;
         State s;
         s.tid = threadIdx.x;
         s.wave = __builtin_amdgcn_readfirstlane(s.tid >> 6);
@@ -871,9 +961,10 @@ struct Gemm {
         // robin, so tile j runs on XCD j % 8 (the grid is a multiple of 8);
         // regroup so that each XCD gets a contiguous run of tiles, and order
         // the runs in bands of kGroupM tile-rows so that the tiles one XCD
-        // holds at a time share A rows and B columns in its L2.
+        // holds at a time share A rows and B columns in its L2.  (With
+        // band_order the caller has numbered the tiles that way already.)
         int w = j;
-        if ((ntiles & 7) == 0 && (gridDim.x & 7) == 0) w = (w & 7) * (ntiles >> 3) + (w >> 3);
+        if (!band_order && (ntiles & 7) == 0 && (gridDim.x & 7) == 0) w = (w & 7) * (ntiles >> 3) + (w >> 3);
         constexpr int kGroupM = 4;
         const int band = kGroupM * args.tiles_n;
         const int g = w / band;
@@ -886,15 +977,15 @@ struct Gemm {
 
         s.K = args.K;
         {
-            // K splits are whole BKMAX-wide units, so that every stage count
-            // adds the same k-slices in the same order; the ragged head goes
-            // with the last split.
+            // K splits and stream-K pieces are whole BKMAX-wide units, so
+            // that every stage count adds the same k-slices in the same
+            // order; the ragged head goes with the piece that holds the
+            // tile's last unit.
             constexpr int BKMAX = block_k(DT, TC, 1, VARIANT);
             static_assert(BKMAX % BK == 0 && (BKMAX == BK || STAGES >= 3), "head tiles are all in the prologue");
             const int head = k_head_tiles(args.K, BK, BKMAX);
             const int units = args.K / BKMAX, per = BKMAX / BK;
-            const int u0 = p * units / args.splits, u1 = (p + 1) * units / args.splits;
-            s.head = (p == args.splits - 1) ? head : 0;
+            s.head = last ? head : 0;
             s.nbody = (u1 - u0) * per;
             s.nt = s.nbody + s.head;
             s.tbase = u0 * per;
@@ -915,7 +1006,9 @@ struct Gemm {
             // starts at the same k-slice; every (stages, variant) pair of a
             // call takes the same decision.
             const bool rotate = BM < 256 || args.tiles_m * args.tiles_n * args.splits > (int)gridDim.x;
-            s.rot = (rotate && u1 > u0) ? (int)(((uint32_t)(j & 7) * 9u) % (uint32_t)(u1 - u0)) * per : 0;
+            const uint32_t xcd = band_order ? (blockIdx.x & 7) : (uint32_t)(j & 7);
+            s.rot = rot_u >= 0 ? rot_u * per
+                  : (rotate && u1 > u0) ? (int)((xcd * 9u) % (uint32_t)(u1 - u0)) * per : 0;
         }
         const uint8_t* A = (const uint8_t*)args.A + (int64_t)m0 * args.lda * SZ;
         const uint8_t* B = RR ? (const uint8_t*)args.B + (int64_t)n0 * SZ
@@ -1118,8 +1211,8 @@ struct Gemm {
         }
 
         if constexpr (WK > 1) add_k_groups(s, smem, acc);
-        if (args.splits > 1) {
-            splitk(args, smem, s, acc, p, m0, n0);
+        if (mode != 0) {
+            partial(args, smem, s, acc, mode, part, j, m0, n0);
             return;
         }
 
@@ -1322,7 +1415,8 @@ pipegemm_kernel(GemmArgs args) {
     a.A = args.A; a.B = args.B; a.C = args.C;
     a.lda = args.lda; a.ldb = args.ldb; a.ldc = args.ldc;
     a.M = args.M; a.N = args.N; a.K = args.K;
-    a.tiles_m = args.tiles_m; a.tiles_n = args.tiles_n; a.splits = args.splits; a.ws = args.ws;
+    a.tiles_m = args.tiles_m; a.tiles_n = args.tiles_n; a.splits = args.splits; a.sk_tiles = args.sk_tiles;
+    a.ws = args.ws;
     G::run(a, (uint8_t PG_LDS*)smem_raw);
 }
 

@@ -21,7 +21,8 @@ struct GemmArgs {
     int32_t M, N, K;
     int32_t tiles_m, tiles_n;
     int32_t splits;     // K splits per C tile (1: none)
-    void* ws;           // splits > 1: per-tile arrival counters, then the partial tiles
+    int32_t sk_tiles;   // the last sk_tiles tiles are shared out stream-K over the grid (0: none)
+    void* ws;           // splits > 1 or sk_tiles > 0: per-tile arrival counters, then the partial tiles
 };
 
 struct KernelEntry {

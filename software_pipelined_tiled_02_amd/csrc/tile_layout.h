@@ -264,6 +264,29 @@ constexpr int k_phys_tile(int t, int head, int nbody, int rot) {
     return t < head ? nbody + t : (t - head + rot >= nbody ? t - head + rot - nbody : t - head + rot);
 }
 
+// Stream-K schedule.  The last `sk_tiles` C tiles of a call are cut into
+// units (the class's largest K-tile; a K shorter than one unit is one
+// unit), numbered tile by tile, `total` = sk_tiles x units; workgroup g of
+// G (G <= total) takes units [sk_begin(g), sk_begin(g + 1)).  Its piece of
+// each tile it touches is contiguous.  A tile that several workgroups touch
+// is summed from partial tiles: workgroup g writes the piece that begins
+// its range into partial slot 2g, and a piece that begins at a tile's first
+// unit (and ends inside that tile: the last piece of its range) into slot
+// 2g + 1.  A piece that is a whole tile is stored as C directly.
+constexpr int64_t sk_begin(int64_t g, int64_t G, int64_t total) { return g * total / G; }
+// The workgroup whose range holds unit i (the largest g with sk_begin(g) <= i).
+constexpr int64_t sk_owner(int64_t i, int64_t G, int64_t total) { return ((i + 1) * G + total - 1) / total - 1; }
+// End (a unit of its tile, at most U) of the piece of range [i, e) that
+// starts at unit i: the piece covers units i mod U .. sk_piece_end - 1 of
+// tile i / U.
+constexpr int64_t sk_piece_end(int64_t i, int64_t e, int64_t U) {
+    return (i % U + (e - i) < U) ? i % U + (e - i) : U;
+}
+// Partial slot of workgroup g's piece of the tile whose first unit is t0.
+constexpr int64_t sk_slot(int64_t g, int64_t t0, int64_t G, int64_t total) {
+    return 2 * g + (sk_begin(g, G, total) >= t0 ? 0 : 1);
+}
+
 // Budget check of one instance: LDS ring within the CU's LDS, and every
 // per-lane load count a whole number.
 constexpr bool instance_fits(int dt, int tc, int stages, int variant) {

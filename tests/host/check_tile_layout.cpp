@@ -17,7 +17,13 @@
 //     prologue, and every stage count adds the k-slices in one order;
 //  6. the epilogue strips of 2-byte outputs (strip_off) are written with
 //     16-byte writes and read back without bank conflicts (the measured
-//     8-lane write clocks, the 16-lane read clocks above).
+//     8-lane write clocks, the 16-lane read clocks above);
+//  7. the stream-K schedule (sk_begin, sk_owner, sk_piece_end, sk_slot),
+//     walked as the kernel walks it: every unit of every tile is covered
+//     once, a tile is either one whole piece or partial pieces from the
+//     consecutive workgroups sk_owner names, in K order, each writing the
+//     slot sk_slot gives the finisher, and no two partial pieces share a
+//     slot.
 // Prints one line per chunks-per-row value; exits non-zero on failure.
 #include <cstdio>
 #include <initializer_list>
@@ -402,6 +408,56 @@ int main() {
         }
     std::printf("K splits and rotation: %s\n", split_fail ? "FAIL" : "every tile once, one k-slice order for all stage counts");
     fail += split_fail;
+    // 7. Stream-K schedule.
+    int sk_fail = 0;
+    long long schedules = 0, partial_tiles = 0;
+    for (int64_t tiles = 1; tiles <= 40; tiles += (tiles < 12 ? 1 : 7))
+        for (int64_t U = 1; U <= 13; U += (U < 5 ? 1 : 4))
+            for (int64_t G = 1; G <= 300; G += (G < 20 ? 1 : 37)) {
+                const int64_t total = tiles * U;
+                if (G > total) continue;
+                ++schedules;
+                // pieces[tile] in K order: (workgroup, a, b, slot or -1 for a whole tile)
+                struct Piece { int64_t g, a, b, slot; };
+                static Piece pieces[40][64];
+                int np[40] = {0};
+                static bool slot_used[600];
+                for (int64_t q = 0; q < 2 * G; ++q) slot_used[q] = false;
+                for (int64_t g = 0; g < G; ++g) {
+                    const int64_t i0 = sk_begin(g, G, total), e = sk_begin(g + 1, G, total);
+                    if (e <= i0) ++sk_fail;   // every range non-empty
+                    for (int64_t i = i0; i < e;) {
+                        const int64_t t = i / U, a = i - t * U, b = sk_piece_end(i, e, U);
+                        if (b <= a || b > U) { ++sk_fail; break; }
+                        const bool whole = a == 0 && b == U;
+                        const int64_t slot = whole ? -1 : 2 * g + (i == i0 ? 0 : 1);
+                        if (np[t] < 64) pieces[t][np[t]++] = Piece{g, a, b, slot};
+                        if (!whole) {
+                            if (slot_used[slot]) ++sk_fail;
+                            slot_used[slot] = true;
+                        }
+                        i += b - a;
+                    }
+                }
+                for (int64_t t = 0; t < tiles; ++t) {
+                    const int64_t t0 = t * U, g0 = sk_owner(t0, G, total), g1 = sk_owner(t0 + U - 1, G, total);
+                    int64_t next = 0;
+                    for (int k = 0; k < np[t]; ++k) {
+                        const Piece& pc = pieces[t][k];
+                        if (pc.a != next) ++sk_fail;      // contiguous, in K order
+                        next = pc.b;
+                        if (pc.g != g0 + k) ++sk_fail;    // the owners, in order
+                        if (np[t] > 1 && pc.slot != sk_slot(pc.g, t0, G, total)) ++sk_fail;
+                    }
+                    if (next != U || np[t] != g1 - g0 + 1) ++sk_fail;
+                    if ((np[t] == 1) != (pieces[t][0].slot == -1)) ++sk_fail;
+                    partial_tiles += np[t] > 1;
+                }
+            }
+    std::printf("stream-K schedule: %lld schedules, %lld tiles summed from partials: %s\n", schedules,
+                partial_tiles, sk_fail ? "FAIL" : "every unit once, owners and slots as the finisher reads them");
+    if (partial_tiles == 0) ++sk_fail;
+    fail += sk_fail;
     std::printf(fail ? "FAIL (%d)\n" : "OK\n", fail);
     return fail ? 1 : 0;
 }

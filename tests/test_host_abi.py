@@ -243,3 +243,50 @@ def test_occupancy_rejects_null_handle():
     out = binding.Occupancy()
     import ctypes
     assert lib.gemm_occupancy(None, 256, 256, 256, 3, 0, 2, 0, ctypes.byref(out)) == binding.GEMM_ERR_INVALID_ARG
+
+
+def qs(M=5120, N=5120, K=5120, dtype="bf16", layout="RC", stages=3, variant="direct", tile="auto", grid=0):
+    return binding.gemm_query_streamk(M, N, K, dtype, layout, stages, variant, grid=grid, tile=tile, check=False)
+
+
+def test_streamk_plan():
+    """Stream-K rounds, grid and workspace as the header states."""
+    OK = binding.GEMM_OK
+    part = 256 * 256 * 4
+    # 400 tiles of 256x256 on 256 workgroups: less than two rounds, all stream-K
+    rc, info = qs()
+    assert rc == OK and info["tile"] == binding.GEMM_TILE_256x256 and info["c_tiles"] == 400
+    assert info["sk_tiles"] == 400 and info["grid"] == 256 and info["splits"] == 1
+    assert info["workspace_bytes"] == 65536 + 2 * 256 * part
+    # 1100 tiles (4.3 rounds): three rounds data-parallel, the rest stream-K
+    rc, info = qs(M=256 * 44, N=256 * 25)
+    assert rc == OK and info["c_tiles"] == 1100 and info["sk_tiles"] == 1100 - 3 * 256
+    # an explicit grid; the grid is at most the number of units
+    rc, info = qs(grid=100)
+    assert rc == OK and info["grid"] == 100 and info["sk_tiles"] == 400 - 100 * 3
+    rc, info = qs(M=256, N=256, K=3 * 64, tile="256x256", grid=50)   # one tile of three 64-wide units
+    assert rc == OK and info["grid"] == 3 and info["sk_tiles"] == 1
+    rc, info = qs(M=256, N=256, K=40, tile="256x256", grid=50)       # K below one unit: one unit
+    assert rc == OK and info["grid"] == 1 and info["sk_tiles"] == 1
+    # nothing to do: no stream-K tiles, no workspace
+    rc, info = qs(M=0)
+    assert rc == OK and info["sk_tiles"] == 0 and info["workspace_bytes"] == 0
+    # the tile choice is gemm_run's; the same for every (stages, variant)
+    for stages in (1, 2, 3, 4):
+        for variant in ("reg", "direct"):
+            rc, info = qs(M=1000, N=1000, K=1000, stages=stages, variant=variant)
+            assert rc == OK and info["tile"] == q(M=1000, N=1000, K=1000, stages=stages, variant=variant)[1]["tile"]
+
+
+def test_streamk_arguments():
+    E, U = binding.GEMM_ERR_INVALID_ARG, binding.GEMM_ERR_UNSUPPORTED
+    assert qs(grid=-1)[0] == E
+    # more than 16384 C tiles
+    assert qs(M=8192, N=8192 * 4, K=8192, tile="32x64")[0] == U
+    # partial tiles past 2 GiB: 2 x 4096 x 256 KiB
+    assert qs(M=256 * 64, N=256 * 64, grid=4096)[0] == U
+    assert qs(M=256 * 64, N=256 * 64, grid=4000)[0] == binding.GEMM_OK
+    lib = binding.library()
+    rc = lib.gemm_run_streamk(None, 5120, 5120, 5120, 2, 1, 3, 1, 0, 16, 5120, 16, 5120, 16, 5120,
+                              256, 1 << 30, None)
+    assert rc == E
