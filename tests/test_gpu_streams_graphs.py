@@ -1,7 +1,8 @@
 """The C ABI on streams other than the default one, and inside a captured
-graph: gemm_run and gemm_run_splitk enqueue only kernel launches (no memory
-set-up or copies), so a graph that captures them replays them; the split-K
-arrival counters come back to zero after each replay.  Every replay runs on
+graph: gemm_run, gemm_run_splitk and gemm_run_streamk enqueue only kernel
+launches (no memory set-up or copies), so a graph that captures them replays
+them; the split-K / stream-K arrival counters come back to zero after each
+replay.  Every replay runs on
 new inputs copied into the captured buffers (with eager work and
 synchronisation in between) and is checked against the oracle.
 """
@@ -38,18 +39,25 @@ def test_side_stream(g, dtype):
     check_close(c.cpu(), ref, dtype, "side stream")
 
 
-def _graph_case(g, dtype, splits, tile):
+def _graph_case(g, dtype, splits, tile, sk_grid=None):
     M, N, K = 384, 320, 2048
     out_dt = inputs.OUT_TORCH_DTYPES[dtype]
     g.set_tile(tile)
     a0, b0 = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=0)
     da, db = a0.cuda(), b0.cuda()
     c = torch.zeros((M, N), dtype=out_dt, device="cuda")
-    _, info = binding.gemm_query(M, N, K, dtype, "RC", 3, "direct", tile=tile, splits=splits)
+    if sk_grid is None:
+        _, info = binding.gemm_query(M, N, K, dtype, "RC", 3, "direct", tile=tile, splits=splits)
+    else:
+        _, info = binding.gemm_query_streamk(M, N, K, dtype, "RC", 3, "direct", grid=sk_grid, tile=tile)
+        assert info["sk_tiles"] > 0
     ws = g.workspace(info["workspace_bytes"]) if info["workspace_bytes"] else None
 
     def call(stream):
-        if splits == 1:
+        if sk_grid is not None:
+            binding.gemm_run_streamk(g.h, M, N, K, dtype, "RC", 3, "direct", sk_grid, da, K, db, K, c, N,
+                                     ws, ws.numel(), stream=stream)
+        elif splits == 1:
             binding.gemm_run(g.h, M, N, K, dtype, "RC", 3, "direct", da, K, db, K, c, N, stream=stream)
         else:
             binding.gemm_run_splitk(g.h, M, N, K, dtype, "RC", 3, "direct", splits, da, K, db, K, c, N,
@@ -88,3 +96,9 @@ def test_graph_replay(g, dtype):
 @pytest.mark.parametrize("dtype", ("i8", "bf16"))
 def test_graph_replay_splitk(g, dtype):
     _graph_case(g, dtype, 4, "128x128")
+
+
+@pytest.mark.parametrize("dtype", ("i8", "f16"))
+def test_graph_replay_streamk(g, dtype):
+    # 9 tiles of 128x128 over 5 workgroups: tiles summed from partials
+    _graph_case(g, dtype, 1, "128x128", sk_grid=5)
