@@ -3,7 +3,8 @@
 Small ragged shapes at every tile class, layout, dtype, stage count and
 variant, with grids that cut tiles into pieces of every kind (a tile from
 one workgroup, a tile summed from two or more, a workgroup's range ending
-and starting inside one tile); for a fixed grid all (stages, variant) pairs
+and starting inside one tile; workgroups numbered XCD by XCD when the grid
+is a multiple of 8); for a fixed grid all (stages, variant) pairs
 must agree bit for bit, since the pieces are whole units of the class's
 largest K-tile and the partial tiles are added in K order.  Then shapes
 whose tiles fill no whole number of rounds (the partial last wave stream-K
@@ -62,7 +63,7 @@ def test_streamk_all_stages_variants(g, dtype, layout, tile):
     ad, bd = a.cuda(), b.cuda()
     g.set_tile(tile)
     try:
-        for grid in (2, 5, 7, 23):
+        for grid in (2, 5, 16, 23):      # 16: workgroups numbered XCD by XCD
             first = None
             for stages in (1, 2, 3, 4):
                 for variant in ("reg", "direct"):
@@ -115,6 +116,31 @@ def test_streamk_after_data_parallel_rounds(g, dtype):
             assert info["c_tiles"] == 64 and info["sk_tiles"] == 64 - 3 * 14 and info["grid"] == 14, info
             check_sentinel(c, M, N, dtype)
             check_close(c[:M, :N], ref, dtype, "DP + SK S=%d %s" % (stages, variant))
+            if first is None:
+                first = c
+            else:
+                assert torch.equal(c.view(torch.uint8), first.view(torch.uint8))
+        assert counters_zero(g)
+    finally:
+        g.set_tile("auto")
+
+
+@pytest.mark.parametrize("dtype", ("i8", "bf16"))
+def test_streamk_unaligned_k(g, dtype):
+    """The register-staged variant's ragged-K instances (K not whole 16-byte
+    chunks) under stream-K."""
+    M, N, K = 200, 96, 1501
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=8)
+    ref = oracle_full(a, b, dtype, "RC")
+    ad, bd = a.cuda(), b.cuda()
+    g.set_tile("128x128")
+    try:
+        first = None
+        for stages in (1, 2, 3, 4):
+            c, info = run_sk(g, ad, bd, dtype, "RC", stages, "reg", M, N, K, 3)
+            assert info["sk_tiles"] > 0
+            check_sentinel(c, M, N, dtype)
+            check_close(c[:M, :N], ref, dtype, "%s K=%d S=%d stream-K" % (dtype, K, stages))
             if first is None:
                 first = c
             else:
