@@ -116,3 +116,41 @@ def test_widened_inputs_give_the_same_doubles(orc, dtype, layout):
     ref = orc.gemm(inputs.to_oracle(a, dtype), inputs.to_oracle(b, dtype), dtype, layout)
     wid = orc.gemm(a.float().contiguous().numpy(), b.float().contiguous().numpy(), "f32", layout)
     assert np.array_equal(ref.view(np.int64), wid.view(np.int64))
+
+
+_THREADS_PROBE = r"""
+import sys, numpy as np
+sys.path.insert(0, %r)
+import oracle
+orc = oracle.OracleLib(oracle.lib_path())
+rng = np.random.default_rng(11)
+out = [orc.num_threads()]
+for dtype, layout in (("f32", "RR"), ("f32", "RC"), ("i8", "RC")):
+    if dtype == "f32":
+        a = rng.uniform(-1, 1, (67, 301)).astype(np.float32)
+        b = rng.uniform(-1, 1, (301, 45) if layout == "RR" else (45, 301)).astype(np.float32)
+    else:
+        a = rng.integers(-128, 128, (67, 301)).astype(np.int8)
+        b = rng.integers(-128, 128, (45, 301)).astype(np.int8)
+    out.append(orc.gemm(a, b, dtype, layout).tobytes().hex())
+print(repr(out))
+"""
+
+
+def test_oracle_threads_do_not_change_the_result(orc):
+    """oracle_num_threads reports the OpenMP threads the oracle runs with
+    (the core count the CPU baseline states), and the result is the same
+    bits with one thread or several: each C element is one sequential sum
+    in increasing k whichever thread computes it."""
+    import ast
+    import subprocess
+    import sys
+    from tests.conftest import ROOT
+    got = {}
+    for n in (1, 3):
+        env = dict(os.environ, OMP_NUM_THREADS=str(n))
+        r = subprocess.run([sys.executable, "-c", _THREADS_PROBE % ROOT], env=env, capture_output=True,
+                           text=True, timeout=120, check=True)
+        got[n] = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+        assert got[n][0] == n, (n, got[n][0])
+    assert got[1][1:] == got[3][1:]
