@@ -55,9 +55,10 @@
  *     each a tile in flight; stages = 1 is the skill's register-only prefetch
  *     into a single buffer (step 1, "if it fails"), stages = 2 the classic
  *     double buffer.
- *   For a fixed dtype, layout and tile every (stages, variant) pair issues
- *   the same matrix-core instructions in the same k order, so all of them
- *   return bit-identical C.
+ *   For a fixed dtype, layout and tile every (stages, variant) pair adds
+ *   the same products in the same k order (the instances built from 16x16
+ *   matrix-core blocks as well as those built from 32x32 ones), so all of
+ *   them return bit-identical C.
  *
  * Memory ownership.  The caller allocates, owns and frees A, B, C and the
  * stream; they are device pointers (hipMalloc or torch CUDA tensors) on the
