@@ -150,6 +150,18 @@ def test_streamk_unaligned_k(g, dtype):
         g.set_tile("auto")
 
 
+@pytest.mark.parametrize("dtype", ("i8", "f32"))
+def test_streamk_k_zero(g, dtype):
+    """K = 0: every tile is one (empty) unit and C = 0."""
+    M, N, K = 300, 200, 0
+    a, b = inputs.make_operands(M, N, K, dtype, "RC", DIST[dtype], seed=1)
+    c, info = run_sk(g, a.cuda(), b.cuda(), dtype, "RC", 2, "direct", M, N, K, 7)
+    assert info["sk_tiles"] > 0 and info["grid"] <= 7, info
+    check_sentinel(c, M, N, dtype)
+    assert int(c[:M, :N].view(torch.uint8).count_nonzero()) == 0
+    assert counters_zero(g)
+
+
 # Partial last waves at full size, automatic tile and grid (one workgroup
 # per CU): (M, N, K, dtype, dist, scale)
 PARTIAL_WAVE = {
