@@ -242,6 +242,51 @@ def gemm_query_streamk(M, N, K, dtype, layout, stages, variant, grid=0, tile="au
     return rc, info.as_dict()
 
 
+_HANDLES = {}   # device index -> Gemm, for run()
+
+
+def run(a, b, *, layout="RC", stages=2, variant="direct", out=None, stream=None):
+    """C = A * B on torch CUDA tensors through gemm_run.
+
+    A is M x K row-major; B is K x N row-major for layout "RR", or its N x K
+    transpose (B column-major) for "RC".  The element type is A's (int8,
+    float16, bfloat16 or float32; B must match); C is int32 for int8 and A's
+    type otherwise.  `out` (M x N, unit stride along the last axis) is
+    written in place, else a new tensor is allocated.  The call is enqueued
+    on `stream` (the current stream of A's device by default) and C is
+    returned.  Argument errors raise ValueError before any HIP call."""
+    import torch
+    names = {torch.int8: "i8", torch.float16: "f16", torch.bfloat16: "bf16", torch.float32: "f32"}
+    outs = {"i8": torch.int32, "f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    if not (isinstance(a, torch.Tensor) and isinstance(b, torch.Tensor)) or a.dim() != 2 or b.dim() != 2:
+        raise ValueError("A and B must be 2-D torch tensors")
+    if a.dtype not in names or b.dtype != a.dtype:
+        raise ValueError("A and B must share one of int8, float16, bfloat16, float32 (got %s, %s)"
+                         % (a.dtype, b.dtype))
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("A and B must be CUDA tensors on one device")
+    dtype = names[a.dtype]
+    M, K = a.shape
+    if _enum(layout, LAYOUTS) == GEMM_LAYOUT_RR:
+        Kb, N = b.shape
+    else:
+        N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ: A has K = %d, B has %d" % (K, Kb))
+    if out is None:
+        out = torch.empty((M, N), dtype=outs[dtype], device=a.device)
+    elif (not isinstance(out, torch.Tensor) or out.dtype != outs[dtype] or tuple(out.shape) != (M, N)
+          or out.device != a.device):
+        raise ValueError("out must be an M x N %s tensor on A's device" % outs[dtype])
+    dev = a.device.index if a.device.index is not None else torch.cuda.current_device()
+    g = _HANDLES.get(dev)
+    if g is None:
+        g = _HANDLES[dev] = Gemm(dev)
+    g.run(a, b, out, dtype, layout, stages, variant,
+          stream if stream is not None else torch.cuda.current_stream(a.device))
+    return out
+
+
 class Gemm:
     """Owns a handle; ``run`` takes torch CUDA tensors in the ABI's storage:
     A (M x K row-major), B (K x N row-major for RR, its N x K transpose for

@@ -290,3 +290,13 @@ def test_streamk_arguments():
     rc = lib.gemm_run_streamk(None, 5120, 5120, 5120, 2, 1, 3, 1, 0, 16, 5120, 16, 5120, 16, 5120,
                               256, 1 << 30, None)
     assert rc == E
+
+
+def test_run_rejects_bad_tensors_without_gpu():
+    """binding.run checks its tensors before any HIP call."""
+    import torch
+    a = torch.zeros(4, 8, dtype=torch.bfloat16)
+    b = torch.zeros(5, 8, dtype=torch.bfloat16)
+    for args in ((a, b), (a, b.half()), (a.double(), b.double()), (a, b[:, :4]), (a[0], b)):
+        with pytest.raises(ValueError):
+            binding.run(*args)
