@@ -54,9 +54,10 @@
 // load_k_tail.)  Tiles past the last one get an out-of-range scalar offset
 // and load zeros.  Stores are masked.
 //
-// Split K (splitk): the same kernel, given a split count above 1, runs one
-// K range of a C tile per workgroup and combines the partial tiles through
-// a workspace; with a split count of 1 it is the plain GEMM.
+// Split K and stream-K (run, partial): the same kernel, given a split
+// count above 1, runs one K range of a C tile per workgroup, or, given
+// stream-K tiles, shares their K units out over the grid; the partial tiles
+// are combined through a workspace.  With neither it is the plain GEMM.
 #ifndef PIPEGEMM_GEMM_KERNEL_H
 #define PIPEGEMM_GEMM_KERNEL_H
 
