@@ -59,6 +59,8 @@ WORKLOADS = {
                        "bf16 GEMM M=N=8192 K=8200 (ragged last K-tile), fp32 accumulate, bf16 out"),
     "fp32_256": (256, 256, 256, "f32", "RR", "uniform", 1.0, "mfma",
                  "fp32 GEMM M=N=K=256, A and B row-major"),
+    "fp32_4096_rr": (4096, 4096, 4096, "f32", "RR", "uniform", 1.0, "mfma",
+                     "fp32 GEMM M=N=K=4096, A and B row-major (the fp32 comparison at a compute-bound size)"),
     "fp16_4096_rr": (4096, 4096, 4096, "f16", "RR", "normal", 1.0 / 64.0, "mfma",
                      "fp16 GEMM M=N=K=4096, A and B row-major (B read with transposing LDS reads)"),
     "int8_4096_rr": (4096, 4096, 4096, "i8", "RR", "int", 1.0, "mfma",

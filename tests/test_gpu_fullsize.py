@@ -36,6 +36,8 @@ WORKLOADS = {
     # layout RR at the 256x256 tile (B fragments by transposing LDS reads)
     "fp16_4096_rr": (4096, 4096, 4096, "f16", "RR", "normal", 1.0 / 64.0, False),
     "int8_4096_rr": (4096, 4096, 4096, "i8", "RR", "int", 1.0, False),
+    # the fp32 comparison at a compute-bound size (B element reads)
+    "fp32_4096_rr": (4096, 4096, 4096, "f32", "RR", "uniform", 1.0, False),
 }
 
 
